@@ -70,7 +70,9 @@ def build_permutation(topk_ids, num_experts: int, m_alloc: int | None = None):
     if m_alloc is None:
         m_alloc = default_m_alloc(num_tokens, top_k, num_experts)
     flat = ids.reshape(-1)
-    counts = np.bincount(flat, minlength=num_experts)[:num_experts]
+    # ids outside [0, E) are routed nowhere (the page does not define them); they get row -1
+    valid = (flat >= 0) & (flat < num_experts)
+    counts = np.bincount(flat[valid], minlength=num_experts)[:num_experts]
     padded = (counts + BLOCK - 1) // BLOCK * BLOCK
     offsets = np.concatenate([[0], np.cumsum(padded)[:-1]]).astype(np.int64)
     m_pad = int(padded.sum())
@@ -78,7 +80,7 @@ def build_permutation(topk_ids, num_experts: int, m_alloc: int | None = None):
         raise ValueError("m_alloc too small for this routing")
     m_indices = np.full(m_alloc, -1, dtype=np.int32)
     src_token = np.full(m_alloc, -1, dtype=np.int32)
-    row_of_entry = np.empty(flat.size, dtype=np.int64)
+    row_of_entry = np.full(flat.size, -1, dtype=np.int64)
     for e in range(num_experts):
         entries = np.nonzero(flat == e)[0]            # ascending entry index = (token, slot) order
         rows = offsets[e] + np.arange(entries.size)
@@ -111,13 +113,15 @@ def silu_mul(y):
 
 
 def combine(y2, row_of_entry, topk_weights):
-    """out[t] = sum_slot w[t, slot] * y2[row_of_entry[t, slot]] in float64."""
+    """out[t] = sum_slot w[t, slot] * y2[row_of_entry[t, slot]] in float64; row -1 adds nothing."""
     y2 = np.asarray(y2, dtype=np.float64)
     rows = np.asarray(row_of_entry, dtype=np.int64)
     w = np.asarray(topk_weights, dtype=np.float64)
     out = np.zeros((rows.shape[0], y2.shape[1]), dtype=np.float64)
     for slot in range(rows.shape[1]):
-        out += w[:, slot:slot + 1] * y2[rows[:, slot]]
+        r = rows[:, slot]
+        live = r >= 0
+        out[live] += w[live, slot:slot + 1] * y2[r[live]]
     return out
 
 

@@ -81,6 +81,16 @@ def test_permutation_with_an_expert_that_gets_no_rows():
     assert p["offsets"].tolist() == [0, 128, 128] and p["m_pad"] == 256
 
 
+def test_permutation_drops_ids_outside_the_expert_range():
+    ids = np.array([[0, 5], [-1, 1], [1, 0]], dtype=np.int32)
+    p = moe.build_permutation(ids, 2)
+    assert p["counts"].tolist() == [2, 2]
+    assert p["row_of_entry"].tolist() == [[0, -1], [-1, 128], [129, 1]]
+    out = moe.combine(np.arange(2 * 256, dtype=np.float64).reshape(256, 2), p["row_of_entry"],
+                      np.ones((3, 2), np.float32))
+    assert out[0].tolist() == [0.0, 1.0] and out[1].tolist() == [256.0, 257.0]
+
+
 def test_silu_mul_closed_forms():
     y = np.array([[0.0, 1.0, 40.0, -40.0, 5.0, 3.0, 2.0, 7.0]])
     h = moe.silu_mul(y)[0]
