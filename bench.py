@@ -1,0 +1,223 @@
+"""Benchmark of the FP8 groupwise GEMM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--configs]
+
+The headline line times the plain 4096x4096x7168 groupwise GEMM (E4M3 inputs, 1x128 / 128x128
+FP32 scales, BF16 out): W untimed launches, then exactly K launches bracketed by synchronisations,
+timed with HIP events on the stream the kernel is launched on. value = algorithmic TFLOP/s
+(2*m*n*k per launch). ``roofline`` prices that against the dense FP8 matrix-core peak; ``traffic``
+comes from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary when it was taken on the current
+kernel source, else null. ``cpu_baseline`` times the float64 CPU oracle on a bounded row sample of
+the same workload.
+
+--configs adds the other workloads (contiguous grouped over 32 Zipf-sized experts, masked batched
+over 16 groups, the 4096-token expert FFN), each timed per launch with the caches flushed in
+between, under "configs".
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP8_DENSE_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 matrix-core peak
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_plain_4096x4096x7168.json")
+KERNEL_SOURCE = os.path.join(ROOT, "moe_expert_matmul_amd", "csrc", "gemm.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic():
+    """Measured HBM bytes per launch, if the committed counters match the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def time_back_to_back(fn, steps: int, warmup: int):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(stop) / steps, wall
+
+
+def time_cold(fn, steps: int, warmup: int, flush):
+    """Median per-launch time with a cache-flushing write between launches (not timed)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(steps):
+        flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    times.sort()
+    return times[len(times) // 2], times[0]
+
+
+def cpu_baseline(d, flops_per_row):
+    """Oracle on a bounded row sample of the plain workload (inputs are the GPU's bytes)."""
+    import numpy as np
+    import workloads
+    from oracle import gemm as ogemm
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"),
+                      default=1)
+    except Exception:  # threadpoolctl missing: numpy's BLAS uses every core by default
+        threads = os.cpu_count()
+    rows = 192
+    a = workloads.to_numpy(d["a"][:rows])
+    sa = workloads.to_numpy(d["a_scale"][:rows])
+    b = workloads.to_numpy(d["b"])
+    sb = workloads.to_numpy(d["b_scale"])
+    t0 = time.perf_counter()
+    ogemm.gemm_fp8_nt_groupwise(a, b, sa, sb)
+    dt = time.perf_counter() - t0
+    return {"value": round(rows * flops_per_row / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {rows} of 4096 rows x all 4096 columns x k=7168 of the plain workload "
+                      f"({rows * flops_per_row / 1e9:.1f} GFLOP, {dt:.1f} s, float64 BLAS per 128-wide K block)"}
+
+
+def other_configs(steps, warmup):
+    import numpy as np
+    import torch
+    import moe_expert_matmul_amd as fp8g
+    import workloads
+    dev = torch.device("cuda")
+    scratch = torch.empty(1 << 29, dtype=torch.uint8, device=dev)  # 512 MB: evicts L2 and the MALL
+    flush = lambda: scratch.fill_(1)
+    res = {}
+
+    d = workloads.contiguous(32, 8192, 4096, 7168, 1.1, seed=0, device=dev)
+    out = torch.empty((d["m"], d["n"]), dtype=torch.bfloat16, device=dev)
+    fn = lambda: fp8g.fp8_group_gemm_contiguous(d["a"], d["b"], d["a_scale"], d["b_scale"], d["m_indices"], out)
+    med, best = time_cold(fn, steps, warmup, flush)
+    valid = int(d["counts"].sum())
+    flops = 2.0 * valid * 4096 * 7168
+    hbm = d["a"].numel() + d["b"].numel() + 4 * (d["a_scale"].numel() + d["b_scale"].numel()) + d["m"] * 4 \
+        + 2 * valid * 4096
+    res["contiguous_32experts_8192rows_n4096_k7168"] = {
+        "ms": round(med, 4), "ms_best": round(best, 4), "tflops": round(flops / med / 1e9, 2),
+        "hbm_gbs": round(hbm / med / 1e6, 1), "frac_hbm": round(hbm / med / 1e6 / HBM_PEAK_GBS, 4),
+        "frac_mfma": round(flops / med / 1e9 / FP8_DENSE_PEAK_TFLOPS, 4), "m_pad": d["m"], "valid_rows": valid}
+    del d, out
+
+    d = workloads.masked(16, 256, 4096, 7168, 128, seed=0, device=dev)
+    out = torch.empty((16, 256, 4096), dtype=torch.bfloat16, device=dev)
+    fn = lambda: fp8g.fp8_batch_gemm_masked(d["a"], d["b"], d["a_scale"], d["b_scale"], d["masked_m"], 128, out)
+    med, best = time_cold(fn, steps, warmup, flush)
+    mm = workloads.to_numpy(d["masked_m"]).astype(np.int64)
+    live = mm > 0
+    flops = 2.0 * mm.sum() * 4096 * 7168
+    hbm = mm.sum() * 7168 * 1.0 + live.sum() * 4096 * 7168 + 2 * mm.sum() * 4096 + 4 * (mm.sum() * 56 + live.sum() * 32 * 56)
+    res["masked_16groups_maxm256_n4096_k7168"] = {
+        "ms": round(med, 4), "ms_best": round(best, 4), "tflops": round(flops / med / 1e9, 2),
+        "hbm_gbs": round(hbm / med / 1e6, 1), "frac_hbm": round(hbm / med / 1e6 / HBM_PEAK_GBS, 4),
+        "frac_mfma": round(flops / med / 1e9 / FP8_DENSE_PEAK_TFLOPS, 4), "sum_masked_m": int(mm.sum())}
+    del d, out
+
+    d = workloads.moe(seed=0, device=dev)
+    ws = fp8g.MoeWorkspace.allocate(4096, 8, 64, 7168, 2048, dev)
+    out = torch.empty((4096, 7168), dtype=torch.bfloat16, device=dev)
+    fn = lambda: fp8g.moe_ffn_fp8_block_scale(d["x"], d["topk_ids"], d["topk_weights"], d["w1"], d["s1"],
+                                              d["w2"], d["s2"], out=out, workspace=ws)
+    med, best = time_cold(fn, steps, warmup, flush)
+    rows = 4096 * 8
+    flops = 2.0 * rows * 4096 * 7168 + 2.0 * rows * 7168 * 2048
+    res["moe_ffn_4096tok_h7168_e64_top8_i2048"] = {
+        "ms": round(med, 4), "ms_best": round(best, 4), "tflops": round(flops / med / 1e9, 2),
+        "frac_mfma": round(flops / med / 1e9 / FP8_DENSE_PEAK_TFLOPS, 4)}
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--configs", action="store_true", help="also time the grouped, masked and expert-FFN workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU sharding is not built",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_expert_matmul_amd as fp8g
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    m = n = 4096
+    k = 7168
+    d = workloads.plain(m, n, k, seed=0, device=dev)
+    out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    fn = lambda: fp8g.fp8_gemm_nt_groupwise(d["a"], d["b"], d["a_scale"], d["b_scale"], out)
+    ms, wall = time_back_to_back(fn, args.steps, args.warmup)
+    flops = 2.0 * m * n * k
+    tflops = flops / ms / 1e9
+    line = {
+        "metric": "FP8 groupwise GEMM TFLOP/s and % of MI355X dense-FP8 MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3 (fp32 accumulate, bf16 out)",
+        "data": "synthetic: N(0,1) quantised to E4M3 per 1x128 (a) / 128x128 (b) block, seed 0",
+        "config": {"workload": "plain FP8 NT groupwise GEMM m=4096 n=4096 k=7168, K-major FP32 scales, BF16 out",
+                   "m": m, "n": n, "k": k},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": FP8_DENSE_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / FP8_DENSE_PEAK_TFLOPS, 4),
+                     "traffic": load_traffic()},
+        "wall_s_timed_region": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(d, 2.0 * n * k)
+    if args.configs:
+        del d, out
+        torch.cuda.empty_cache()
+        line["configs"] = other_configs(max(5, args.steps // 5), 2)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,186 @@
+/*
+ * fp8g -- FP8 (E4M3) groupwise-scaled NT GEMM for MoE expert layers, native to AMD MI355X (gfx950).
+ *
+ * C ABI of libfp8g.so. Every entry point takes plain device pointers and sizes and returns a status;
+ * no PyTorch (or any other framework) type appears here.
+ *
+ * Conventions shared by every call (flashmla-rs README, section "Design Notes"; flashinfer-rs
+ * README, section "Additional Notes"):
+ *   - Memory is owned by the caller. Every pointer argument is a DEVICE pointer on the current HIP
+ *     device unless it is documented otherwise. The library never allocates, frees or keeps a
+ *     pointer after the call returns.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the call returns
+ *     without synchronising. No call reads device memory from the host.
+ *   - Arguments are validated before anything is launched; C++ exceptions never cross the ABI. A
+ *     failing call returns a non-zero status, launches nothing and leaves a message that
+ *     fp8g_last_error() returns (thread-local, valid until the thread's next fp8g call).
+ *   - An unsupported device (anything but gfx950) is an error (FP8G_NOT_SUPPORTED), never a fallback.
+ *   - Tensors are dense and row-major ("contiguous"); E4M3 means OCP E4M3FN (bias 7, max 448,
+ *     NaN = S.1111.111, no infinities), one byte per element. BF16 outputs are round-to-nearest-even.
+ *   - Pointers must be 16-byte aligned (E4M3 operands, outputs) or 4-byte aligned (scales, indices).
+ *   - Output rows that the operation leaves unspecified are not written.
+ *
+ * Scale granularity: only (gran_m, gran_n, gran_k) = (1, 128, 128) -- one FP32 scale per row and
+ * 128-wide K block of `a`, one per 128x128 block of `b` -- is implemented; any other value returns
+ * FP8G_NOT_SUPPORTED. k must be a multiple of 128 and n a multiple of 128.
+ *
+ * Arithmetic (MATE FlashInfer-API page, section "GEMM"): for every output element
+ *     out[i][j] = bf16( sum_kb  sa(i,kb) * sb(j/128,kb) * sum_{k in block kb} a[i][k] * b[j][k] )
+ * where each 128-wide block sum is one FP8 matrix-core product accumulated in FP32 and the scale
+ * product is applied by one FP32 multiply-add per K block. Results do not depend on `expected_m`
+ * or on the tile configuration the library picks.
+ */
+#ifndef FP8G_H_
+#define FP8G_H_
+
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define FP8G_API __attribute__((visibility("default")))
+#else
+#define FP8G_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP8G_OK = 0,
+  FP8G_INVALID_ARGUMENT = 1, /* null pointer, bad size, misalignment, bad enum value */
+  FP8G_NOT_SUPPORTED = 2,    /* unsupported granularity, or the device is not gfx950 */
+  FP8G_HIP_ERROR = 3,        /* the HIP runtime reported an error (message has hipGetErrorString) */
+  FP8G_INTERNAL = 4          /* an unexpected C++ exception inside the library */
+} fp8g_status_t;
+
+typedef enum {
+  FP8G_SCALE_K_MAJOR = 0,  /* a_scale (m, k/128), b_scale (n/128, k/128) */
+  FP8G_SCALE_MN_MAJOR = 1  /* a_scale (k/128, m), b_scale (k/128, n/128) */
+} fp8g_scale_major_t;
+
+/* Message of the calling thread's last failing call ("" after a successful one). */
+FP8G_API const char* fp8g_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+FP8G_API int32_t fp8g_version(void);
+
+/*
+ * Plain form: out = a @ b.T with groupwise scales.
+ * MATE FlashInfer-API page, section "GEMM", gemm_fp8_nt_groupwise.
+ *   a        (m, k)  E4M3, row-major
+ *   b        (n, k)  E4M3, row-major (the product is a @ b.T)
+ *   a_scale  FP32, (m, k/128) when scale_major = K-major, (k/128, m) when MN-major
+ *   b_scale  FP32, (n/128, k/128) when K-major, (k/128, n/128) when MN-major
+ *   out      (m, n)  BF16, fully written
+ * m >= 0 is arbitrary; n and k are multiples of 128. m == 0 or n == 0 is a no-op; k == 0 writes
+ * zeros. scale_major applies to both scale tensors.
+ */
+FP8G_API fp8g_status_t fp8_gemm_nt_groupwise(const void* a, const void* b, const float* a_scale,
+                                    const float* b_scale, void* out, int64_t m, int64_t n,
+                                    int64_t k, int32_t scale_major, int32_t gran_m,
+                                    int32_t gran_n, int32_t gran_k, void* stream);
+
+/*
+ * Contiguous grouped form: out[i] = a[i] @ b[m_indices[i]].T for every row with m_indices[i] >= 0.
+ * MATE FlashInfer-API page, section "GEMM", group_deepgemm_fp8_nt_groupwise.
+ *   a          (m, k)              E4M3; m is a multiple of 128
+ *   b          (num_groups, n, k)  E4M3 expert weights
+ *   a_scale    FP32, (m, k/128) K-major, or (k/128, m) MN-major
+ *   b_scale    FP32, (num_groups, n/128, k/128) K-major, or (num_groups, k/128, n/128) MN-major
+ *   m_indices  (m,) int32 expert of every row; -1 marks a padding row. Each expert's rows occupy a
+ *              contiguous, 128-row-aligned region, so every aligned 128-row tile holds one expert
+ *              and padding. The tile's expert is the largest index among its rows.
+ *   out        (m, n) BF16; rows whose m_indices is -1 (or is not the tile's expert) are not
+ *              written.
+ * Indices outside [-1, num_groups) are treated as padding. The MN-major layout is an extension
+ * (the page defines the grouped forms with K-major scales only).
+ */
+FP8G_API fp8g_status_t fp8_group_gemm_contiguous(const void* a, const void* b, const float* a_scale,
+                                        const float* b_scale, const int32_t* m_indices, void* out,
+                                        int64_t m, int64_t n, int64_t k, int64_t num_groups,
+                                        int32_t scale_major, int32_t gran_m, int32_t gran_n,
+                                        int32_t gran_k, void* stream);
+
+/*
+ * Masked batched form: out[g, :masked_m[g]] = a[g, :masked_m[g]] @ b[g].T.
+ * MATE FlashInfer-API page, section "GEMM", batch_deepgemm_fp8_nt_groupwise.
+ *   a          (num_groups, max_m, k)  E4M3
+ *   b          (num_groups, n, k)      E4M3
+ *   a_scale    FP32, (num_groups, max_m, k/128) K-major, or (num_groups, k/128, max_m) MN-major
+ *   b_scale    FP32, (num_groups, n/128, k/128) K-major, or (num_groups, k/128, n/128) MN-major
+ *   masked_m   (num_groups,) int32 valid rows per group, read on the device; values are clamped
+ *              into [0, max_m]
+ *   expected_m host-side hint of the typical masked_m, used only to pick a tile configuration
+ *   out        (num_groups, max_m, n) BF16; rows at or beyond masked_m[g] are not written
+ */
+FP8G_API fp8g_status_t fp8_batch_gemm_masked(const void* a, const void* b, const float* a_scale,
+                                    const float* b_scale, const int32_t* masked_m,
+                                    int64_t expected_m, void* out, int64_t num_groups,
+                                    int64_t max_m, int64_t n, int64_t k, int32_t scale_major,
+                                    int32_t gran_m, int32_t gran_n, int32_t gran_k, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Expert-FFN steps around the grouped GEMM (flashinfer-rs README, section "API Example: Fused MoE
+ * FP8 (cudarc)", DeepSeek FP8 block-scale mode: BF16 tokens, int32 token_selected
+ * (num_tokens, top_k), fc1 weights (num_experts, 2*inter, hidden) holding gate then up rows, fc2
+ * weights (num_experts, hidden, inter), hidden and inter multiples of 128).
+ * ------------------------------------------------------------------------------------------- */
+
+/*
+ * Group the (token, slot) entries of topk_ids by expert into the contiguous grouped layout.
+ *   topk_ids      (num_tokens, top_k) int32 expert ids in [0, num_experts); other values are
+ *                 dropped (routed nowhere)
+ *   m_indices     (m_alloc,) int32 out: expert e owns rows [off_e, off_e + ceil(c_e/128)*128) in
+ *                 expert order (off_0 = 0), where c_e is its entry count; the first c_e rows hold
+ *                 its entries in ascending (token, slot) order, the rest and every row past the
+ *                 last region are -1
+ *   src_token     (m_alloc,) int32 out: token of each row, -1 for padding
+ *   row_of_entry  (num_tokens, top_k) int32 out: row of each entry, -1 if the entry was dropped
+ * m_alloc must be at least num_tokens*top_k + num_experts*127 (rounded up to 128) so that every
+ * routing fits; it must be a multiple of 128. num_experts <= 1024. Deterministic.
+ */
+FP8G_API fp8g_status_t fp8_moe_build_permutation(const int32_t* topk_ids, int64_t num_tokens,
+                                        int64_t top_k, int64_t num_experts, int64_t m_alloc,
+                                        int32_t* m_indices, int32_t* src_token,
+                                        int32_t* row_of_entry, void* stream);
+
+/*
+ * Quantise BF16 token rows per 1x128 block into the permuted layout:
+ *   for every row r with s = src_token[r] >= 0 and every 128-column block c of x[s]:
+ *     scale[r][c] = amax / 448 (FP32 IEEE division; 1 when the block is all zero)
+ *     a_out[r][c*128 + t] = E4M3_RNE(x[s][c*128 + t] / scale[r][c])
+ *   x        (num_tokens, hidden) BF16
+ *   a_out    (m_alloc, hidden) E4M3 out; a_scale_out (m_alloc, hidden/128) FP32 out (K-major)
+ * Rows with src_token = -1 are not written.
+ */
+FP8G_API fp8g_status_t fp8_moe_gather_quant(const void* x, const int32_t* src_token, int64_t num_tokens,
+                                   int64_t hidden, int64_t m_alloc, void* a_out,
+                                   float* a_scale_out, void* stream);
+
+/*
+ * h = silu(y[:, :inter]) * y[:, inter:] in FP32 (silu(g) = g / (1 + exp(-g))), then the 1x128
+ * quantisation above applied to h.
+ *   y        (rows, 2*inter) BF16 (the fc1 output: gate columns, then up columns)
+ *   m_indices (rows,) int32; rows with m_indices < 0 are skipped (not written)
+ *   a_out    (rows, inter) E4M3 out; a_scale_out (rows, inter/128) FP32 out (K-major)
+ */
+FP8G_API fp8g_status_t fp8_moe_silu_mul_quant(const void* y, const int32_t* m_indices, int64_t rows,
+                                     int64_t inter, void* a_out, float* a_scale_out,
+                                     void* stream);
+
+/*
+ * out[t] = bf16( sum_s topk_weights[t][s] * y[row_of_entry[t][s]] ), summed in FP32 in slot
+ * order; entries with row_of_entry = -1 contribute nothing.
+ *   y             (m_alloc, hidden) BF16 (the fc2 output)
+ *   row_of_entry  (num_tokens, top_k) int32;  topk_weights (num_tokens, top_k) FP32
+ *   out           (num_tokens, hidden) BF16, fully written
+ */
+FP8G_API fp8g_status_t fp8_moe_combine(const void* y, const int32_t* row_of_entry,
+                              const float* topk_weights, int64_t num_tokens, int64_t top_k,
+                              int64_t hidden, int64_t m_alloc, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8G_H_ */

@@ -1,0 +1,25 @@
+"""MI355X-native FP8 (E4M3) groupwise-scaled NT GEMM for MoE experts.
+
+All computation happens in libfp8g.so (hand-written HIP kernels for gfx950 behind a C ABI declared
+in include/fp8g.h); this package only marshals torch tensors into that ABI. Importing it does not
+touch the GPU; the first call loads the library and fails loudly if it has not been built.
+"""
+
+from ._lib import Fp8gError, Fp8gInvalidArgument, Fp8gNotSupported, LIB_PATH, load  # noqa: F401
+from .gemm import (  # noqa: F401
+    batch_deepgemm_fp8_nt_groupwise,
+    fp8_batch_gemm_masked,
+    fp8_gemm_nt_groupwise,
+    fp8_group_gemm_contiguous,
+    gemm_fp8_nt_groupwise,
+    group_deepgemm_fp8_nt_groupwise,
+)
+from .moe import (  # noqa: F401
+    MoeWorkspace,
+    default_m_alloc,
+    moe_build_permutation,
+    moe_combine,
+    moe_ffn_fp8_block_scale,
+    moe_gather_quant,
+    moe_silu_mul_quant,
+)

@@ -1,0 +1,355 @@
+// C ABI of libfp8g.so: argument validation, tile-configuration choice and launch.
+//
+// Conventions (flashmla-rs README, section "Design Notes"): caller-owned memory, work enqueued on
+// the caller's stream without synchronisation, exceptions caught at the boundary and reported as a
+// status plus a thread-local message. Validation happens before any launch (flashmla-rs README,
+// section "flashmla"), and a device other than gfx950 is an error rather than a fallback
+// (flashinfer-rs README, section "Architecture Handling").
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <exception>
+#include <string>
+
+#include "../../include/fp8g.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+struct Failure {
+  fp8g_status_t status;
+};
+
+[[noreturn]] void fail(fp8g_status_t status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  throw Failure{status};
+}
+
+void require(bool cond, const char* fmt, ...) {
+  if (cond) return;
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  throw Failure{FP8G_INVALID_ARGUMENT};
+}
+
+void check_hip(hipError_t e, const char* what) {
+  if (e != hipSuccess) fail(FP8G_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Per-device answer to "is this a gfx950?": 0 unknown, 1 yes, 2 no.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+void check_device() {
+  int dev = -1;
+  check_hip(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) fail(FP8G_NOT_SUPPORTED, "device ordinal %d out of range", dev);
+  int state = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    check_hip(hipGetDeviceProperties(&prop, dev), "hipGetDeviceProperties");
+    state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_ok[dev].store(state, std::memory_order_relaxed);
+    if (state == 2)
+      fail(FP8G_NOT_SUPPORTED, "device %d is %s; this library runs on gfx950 (MI355X) only", dev,
+           prop.gcnArchName);
+  }
+  if (state == 2) fail(FP8G_NOT_SUPPORTED, "device %d is not a gfx950 (MI355X)", dev);
+}
+
+void check_granularity(int32_t gm, int32_t gn, int32_t gk) {
+  if (gm != 1 || gn != 128 || gk != 128)
+    fail(FP8G_NOT_SUPPORTED, "scale granularity (%d,%d,%d) not supported; only (1,128,128)", gm, gn, gk);
+}
+
+void check_scale_major(int32_t sm) {
+  require(sm == FP8G_SCALE_K_MAJOR || sm == FP8G_SCALE_MN_MAJOR, "scale_major must be 0 (K) or 1 (MN), got %d", sm);
+}
+
+constexpr int64_t kInt32Max = 2147483647;
+constexpr int64_t kUint32Max = 4294967295LL;
+
+template <typename F>
+fp8g_status_t guarded(F&& body) {
+  try {
+    g_last_error.clear();
+    body();
+    return FP8G_OK;
+  } catch (const Failure& f) {
+    return f.status;
+  } catch (const std::exception& e) {
+    g_last_error = std::string("internal error: ") + e.what();
+    return FP8G_INTERNAL;
+  } catch (...) {
+    g_last_error = "internal error: unknown exception";
+    return FP8G_INTERNAL;
+  }
+}
+
+// Shapes shared by the three GEMM forms.
+void check_gemm_dims(int64_t rows, int64_t n, int64_t k) {
+  require(rows >= 0 && n >= 0 && k >= 0, "sizes must be non-negative (rows %lld, n %lld, k %lld)",
+          (long long)rows, (long long)n, (long long)k);
+  require(k % 128 == 0, "k (%lld) must be a multiple of 128", (long long)k);
+  require(n % 128 == 0, "n (%lld) must be a multiple of 128", (long long)n);
+  require(rows <= kInt32Max && n <= kInt32Max && k <= kInt32Max, "sizes must fit in int32");
+  require(rows * k <= kUint32Max && n * k <= kUint32Max, "one operand matrix must stay below 4 GiB");
+  require(rows * (k / 128) <= kInt32Max, "a_scale must have fewer than 2^31 elements per group");
+}
+
+void check_operands(const void* a, const void* b, const float* sa, const float* sb, const void* out, int64_t k) {
+  require(a && b && out, "a, b and out must be non-null");
+  require(k == 0 || (sa && sb), "a_scale and b_scale must be non-null");
+  require(aligned(a, 16) && aligned(b, 16) && aligned(out, 16), "a, b and out must be 16-byte aligned");
+  require(aligned(sa, 4) && aligned(sb, 4), "scales must be 4-byte aligned");
+}
+
+void set_scale_strides(fp8g::GemmParams& p, int32_t scale_major, int64_t rows) {
+  const int32_t kb = p.kblocks, nb = p.nblocks;
+  if (scale_major == FP8G_SCALE_K_MAJOR) {
+    p.sa_row_stride = kb;
+    p.sa_kb_stride = 1;
+    p.sb_nb_stride = kb;
+    p.sb_kb_stride = 1;
+  } else {
+    p.sa_row_stride = 1;
+    p.sa_kb_stride = (int32_t)rows;
+    p.sb_nb_stride = 1;
+    p.sb_kb_stride = nb;
+  }
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8g_last_error(void) { return g_last_error.c_str(); }
+
+int32_t fp8g_version(void) { return 100; }  // 0.1.0
+
+fp8g_status_t fp8_gemm_nt_groupwise(const void* a, const void* b, const float* a_scale,
+                                    const float* b_scale, void* out, int64_t m, int64_t n,
+                                    int64_t k, int32_t scale_major, int32_t gran_m,
+                                    int32_t gran_n, int32_t gran_k, void* stream) {
+  return guarded([&] {
+    check_gemm_dims(m, n, k);
+    check_scale_major(scale_major);
+    check_granularity(gran_m, gran_n, gran_k);
+    if (m == 0 || n == 0) return;
+    check_operands(a, b, a_scale, b_scale, out, k);
+    check_device();
+    fp8g::GemmParams p{};
+    p.a = static_cast<const uint8_t*>(a);
+    p.b = static_cast<const uint8_t*>(b);
+    p.sa = a_scale;
+    p.sb = b_scale;
+    p.out = static_cast<uint16_t*>(out);
+    p.m = (int32_t)m;
+    p.n = (int32_t)n;
+    p.k = (int32_t)k;
+    p.kblocks = (int32_t)(k / 128);
+    p.nblocks = (int32_t)(n / 128);
+    p.num_groups = 1;
+    set_scale_strides(p, scale_major, m);
+    const fp8g::TileConfig cfg = m > 128 ? fp8g::TILE_256x256 : fp8g::TILE_128x256;
+    p.tiles_m = (int32_t)ceil_div(m, fp8g::tile_rows(cfg));
+    p.tiles_n = (int32_t)ceil_div(n, fp8g::tile_cols(cfg));
+    p.group_m = 4;
+    const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
+    check_hip(fp8g::launch_gemm(fp8g::MODE_PLAIN, cfg, p, (int)grid, (hipStream_t)stream),
+              "fp8_gemm_nt_groupwise launch");
+  });
+}
+
+fp8g_status_t fp8_group_gemm_contiguous(const void* a, const void* b, const float* a_scale,
+                                        const float* b_scale, const int32_t* m_indices, void* out,
+                                        int64_t m, int64_t n, int64_t k, int64_t num_groups,
+                                        int32_t scale_major, int32_t gran_m, int32_t gran_n,
+                                        int32_t gran_k, void* stream) {
+  return guarded([&] {
+    check_gemm_dims(m, n, k);
+    require(num_groups >= 0 && num_groups <= kInt32Max, "num_groups must be in [0, 2^31)");
+    require(m % 128 == 0, "m (%lld) must be a multiple of 128 (128-row-aligned expert regions)", (long long)m);
+    check_scale_major(scale_major);
+    check_granularity(gran_m, gran_n, gran_k);
+    if (m == 0 || n == 0 || num_groups == 0) return;
+    check_operands(a, b, a_scale, b_scale, out, k);
+    require(m_indices != nullptr && aligned(m_indices, 4), "m_indices must be non-null and 4-byte aligned");
+    check_device();
+    fp8g::GemmParams p{};
+    p.a = static_cast<const uint8_t*>(a);
+    p.b = static_cast<const uint8_t*>(b);
+    p.sa = a_scale;
+    p.sb = b_scale;
+    p.out = static_cast<uint16_t*>(out);
+    p.rowinfo = m_indices;
+    p.m = (int32_t)m;
+    p.n = (int32_t)n;
+    p.k = (int32_t)k;
+    p.kblocks = (int32_t)(k / 128);
+    p.nblocks = (int32_t)(n / 128);
+    p.num_groups = (int32_t)num_groups;
+    p.b_group_stride = n * k;
+    p.sb_group_stride = (n / 128) * (k / 128);
+    set_scale_strides(p, scale_major, m);
+    const fp8g::TileConfig cfg = fp8g::TILE_128x256;  // one expert per 128-row tile
+    p.tiles_m = (int32_t)(m / 128);
+    p.tiles_n = (int32_t)ceil_div(n, fp8g::tile_cols(cfg));
+    p.group_m = p.tiles_m;  // row tiles of one column tile run together and share b in L2
+    const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
+    require(grid <= kInt32Max, "too many tiles");
+    check_hip(fp8g::launch_gemm(fp8g::MODE_CONTIG, cfg, p, (int)grid, (hipStream_t)stream),
+              "fp8_group_gemm_contiguous launch");
+  });
+}
+
+fp8g_status_t fp8_batch_gemm_masked(const void* a, const void* b, const float* a_scale,
+                                    const float* b_scale, const int32_t* masked_m,
+                                    int64_t expected_m, void* out, int64_t num_groups,
+                                    int64_t max_m, int64_t n, int64_t k, int32_t scale_major,
+                                    int32_t gran_m, int32_t gran_n, int32_t gran_k, void* stream) {
+  return guarded([&] {
+    check_gemm_dims(max_m, n, k);
+    require(num_groups >= 0 && num_groups <= 65535, "num_groups must be in [0, 65535]");
+    require(expected_m >= 0, "expected_m must be non-negative");
+    check_scale_major(scale_major);
+    check_granularity(gran_m, gran_n, gran_k);
+    if (max_m == 0 || n == 0 || num_groups == 0) return;
+    check_operands(a, b, a_scale, b_scale, out, k);
+    require(masked_m != nullptr && aligned(masked_m, 4), "masked_m must be non-null and 4-byte aligned");
+    check_device();
+    fp8g::GemmParams p{};
+    p.a = static_cast<const uint8_t*>(a);
+    p.b = static_cast<const uint8_t*>(b);
+    p.sa = a_scale;
+    p.sb = b_scale;
+    p.out = static_cast<uint16_t*>(out);
+    p.rowinfo = masked_m;
+    p.m = (int32_t)max_m;
+    p.n = (int32_t)n;
+    p.k = (int32_t)k;
+    p.kblocks = (int32_t)(k / 128);
+    p.nblocks = (int32_t)(n / 128);
+    p.num_groups = (int32_t)num_groups;
+    p.a_group_stride = max_m * k;
+    p.b_group_stride = n * k;
+    p.sa_group_stride = max_m * (k / 128);
+    p.sb_group_stride = (n / 128) * (k / 128);
+    p.out_group_stride = max_m * n;
+    set_scale_strides(p, scale_major, max_m);
+    // expected_m picks the row tile: one 256-row tile per group reads each b tile once; smaller
+    // expected groups use 128-row tiles so that the second row tile is usually skipped.
+    const fp8g::TileConfig cfg =
+        (max_m > 128 && expected_m > 64) ? fp8g::TILE_256x256 : fp8g::TILE_128x256;
+    p.tiles_m = (int32_t)ceil_div(max_m, fp8g::tile_rows(cfg));
+    p.tiles_n = (int32_t)ceil_div(n, fp8g::tile_cols(cfg));
+    p.group_m = p.tiles_m;
+    const int64_t grid = (int64_t)num_groups * p.tiles_m * p.tiles_n;
+    require(grid <= kInt32Max, "too many tiles");
+    check_hip(fp8g::launch_gemm(fp8g::MODE_MASKED, cfg, p, (int)grid, (hipStream_t)stream),
+              "fp8_batch_gemm_masked launch");
+  });
+}
+
+fp8g_status_t fp8_moe_build_permutation(const int32_t* topk_ids, int64_t num_tokens,
+                                        int64_t top_k, int64_t num_experts, int64_t m_alloc,
+                                        int32_t* m_indices, int32_t* src_token,
+                                        int32_t* row_of_entry, void* stream) {
+  return guarded([&] {
+    require(num_tokens >= 0 && top_k >= 0 && num_experts >= 1 && m_alloc >= 0, "sizes must be non-negative, num_experts >= 1");
+    require(num_experts <= 1024, "num_experts must be at most 1024");
+    require(num_tokens * top_k <= kInt32Max && m_alloc <= kInt32Max, "sizes must fit in int32");
+    require(m_alloc % 128 == 0, "m_alloc must be a multiple of 128");
+    const int64_t need = ceil_div(num_tokens * top_k + num_experts * 127, 128) * 128;
+    require(m_alloc >= need, "m_alloc (%lld) must be at least %lld for this many entries and experts",
+            (long long)m_alloc, (long long)need);
+    if (m_alloc == 0) return;
+    require(m_indices && src_token && (num_tokens * top_k == 0 || (topk_ids && row_of_entry)),
+            "pointers must be non-null");
+    require(aligned(topk_ids, 4) && aligned(m_indices, 4) && aligned(src_token, 4) && aligned(row_of_entry, 4),
+            "pointers must be 4-byte aligned");
+    check_device();
+    check_hip(fp8g::launch_moe_build_permutation(topk_ids, (int)num_tokens, (int)top_k, (int)num_experts,
+                                                 (int)m_alloc, m_indices, src_token, row_of_entry,
+                                                 (hipStream_t)stream),
+              "fp8_moe_build_permutation launch");
+  });
+}
+
+fp8g_status_t fp8_moe_gather_quant(const void* x, const int32_t* src_token, int64_t num_tokens,
+                                   int64_t hidden, int64_t m_alloc, void* a_out,
+                                   float* a_scale_out, void* stream) {
+  return guarded([&] {
+    require(num_tokens >= 0 && hidden >= 0 && m_alloc >= 0, "sizes must be non-negative");
+    require(hidden % 128 == 0, "hidden (%lld) must be a multiple of 128", (long long)hidden);
+    require(m_alloc <= kInt32Max && hidden <= kInt32Max && num_tokens <= kInt32Max, "sizes must fit in int32");
+    if (m_alloc == 0 || hidden == 0) return;
+    require(x && src_token && a_out && a_scale_out, "pointers must be non-null");
+    require(aligned(x, 16) && aligned(a_out, 16) && aligned(a_scale_out, 4) && aligned(src_token, 4),
+            "x and a_out must be 16-byte aligned, src_token and a_scale_out 4-byte aligned");
+    check_device();
+    check_hip(fp8g::launch_moe_gather_quant(static_cast<const uint16_t*>(x), src_token, (int)num_tokens,
+                                            (int)hidden, (int)m_alloc, static_cast<uint8_t*>(a_out), a_scale_out,
+                                            (hipStream_t)stream),
+              "fp8_moe_gather_quant launch");
+  });
+}
+
+fp8g_status_t fp8_moe_silu_mul_quant(const void* y, const int32_t* m_indices, int64_t rows,
+                                     int64_t inter, void* a_out, float* a_scale_out,
+                                     void* stream) {
+  return guarded([&] {
+    require(rows >= 0 && inter >= 0, "sizes must be non-negative");
+    require(inter % 128 == 0, "inter (%lld) must be a multiple of 128", (long long)inter);
+    require(rows <= kInt32Max && inter <= kInt32Max / 2, "sizes must fit in int32");
+    if (rows == 0 || inter == 0) return;
+    require(y && m_indices && a_out && a_scale_out, "pointers must be non-null");
+    require(aligned(y, 16) && aligned(a_out, 16) && aligned(a_scale_out, 4) && aligned(m_indices, 4),
+            "y and a_out must be 16-byte aligned, m_indices and a_scale_out 4-byte aligned");
+    check_device();
+    check_hip(fp8g::launch_moe_silu_mul_quant(static_cast<const uint16_t*>(y), m_indices, (int)rows,
+                                              (int)inter, static_cast<uint8_t*>(a_out), a_scale_out,
+                                              (hipStream_t)stream),
+              "fp8_moe_silu_mul_quant launch");
+  });
+}
+
+fp8g_status_t fp8_moe_combine(const void* y, const int32_t* row_of_entry,
+                              const float* topk_weights, int64_t num_tokens, int64_t top_k,
+                              int64_t hidden, int64_t m_alloc, void* out, void* stream) {
+  return guarded([&] {
+    require(num_tokens >= 0 && top_k >= 0 && hidden >= 0 && m_alloc >= 0, "sizes must be non-negative");
+    require(hidden % 128 == 0, "hidden (%lld) must be a multiple of 128", (long long)hidden);
+    require(num_tokens <= kInt32Max && top_k <= 64 && hidden <= kInt32Max && m_alloc <= kInt32Max,
+            "sizes out of range (top_k must be at most 64)");
+    if (num_tokens == 0 || hidden == 0) return;
+    require(out && (top_k == 0 || (y && row_of_entry && topk_weights)), "pointers must be non-null");
+    require(aligned(y, 16) && aligned(out, 16) && aligned(row_of_entry, 4) && aligned(topk_weights, 4),
+            "y and out must be 16-byte aligned, row_of_entry and topk_weights 4-byte aligned");
+    check_device();
+    check_hip(fp8g::launch_moe_combine(static_cast<const uint16_t*>(y), row_of_entry, topk_weights,
+                                       (int)num_tokens, (int)top_k, (int)hidden, (int)m_alloc,
+                                       static_cast<uint16_t*>(out), (hipStream_t)stream),
+              "fp8_moe_combine launch");
+  });
+}
+
+}  // extern "C"

@@ -1,0 +1,304 @@
+// FP8 (E4M3) groupwise-scaled NT GEMM for CDNA4 (gfx950).
+//
+// Computes, for the three forms of the MATE FlashInfer-API page (section "GEMM":
+// gemm_fp8_nt_groupwise, group_deepgemm_fp8_nt_groupwise, batch_deepgemm_fp8_nt_groupwise),
+//     out[i][j] = bf16( sum_kb sa(i,kb) * sb(j/128,kb) * P_kb[i][j] ),
+//     P_kb[i][j] = sum over the 128 k of K block kb of a[i][k] * b[j][k]
+// with a 1x128 scale per row of a and a 128x128 scale per block of b.
+//
+// Mapping onto the matrix cores: one v_mfma_scale_f32_16x16x128_f8f6f4 covers a 16x16 output
+// block over exactly one 128-wide K block (its own E8M0 block scales are left at 2^0), so every
+// MFMA yields one P_kb sub-block in FP32 which is promoted into the FP32 accumulator with one
+// fused multiply-add by sa*sb. The operands are swapped (the MFMA's row operand is b, its column
+// operand is a) so that each lane holds four outputs of one row i and four consecutive columns j:
+// the promotion then needs a single scale per lane and 16-row group, and the epilogue stores 8
+// contiguous bytes of a row.
+//
+// Data movement per workgroup and K block: the BMx128 slab of a and the BNx128 slab of b go from
+// HBM straight into LDS (global_load_lds_dwordx4, no VGPR staging), double-buffered so the loads of
+// block kb+1 overlap the MFMAs of block kb. Rows are 128 bytes in LDS with their 16-byte chunks
+// XOR-swizzled by (row & 7), so the 16 lanes reading one chunk column of 16 rows hit distinct banks.
+// The swizzle is applied on the global side: lane l of a load writes LDS chunk l of its 1 KB slab
+// and fetches the logical chunk that belongs there.
+//
+// Tile scheduling: the 1-D grid is renumbered so that consecutive tiles run on the same XCD (the
+// hardware deals workgroups round-robin over the 8 XCDs, each with its own L2) and then rasterised
+// in groups of `group_m` row tiles. The masked form maps the grid to (group, row tile, col tile) and
+// drops tiles at or beyond masked_m[g]; the contiguous form reads the tile's 128 m_indices and drops
+// tiles that hold only padding. Rows that are not valid are still computed when they share a wave
+// with valid rows (each output row depends only on its own a row and scale) but never stored.
+#include "internal.h"
+
+namespace fp8g {
+namespace kernels {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int KBLK = 128;         // K-block width = bytes of one row per K block
+constexpr int SLAB_ROWS = 8;      // rows filled by one wave-wide 16-byte-per-lane LDS load
+constexpr int E8M0_ONE = 127;     // 2^0 as an E8M0 block scale
+constexpr int FMT_E4M3 = 0;       // f8f6f4 operand format code of FP8 E4M3
+
+template <int BM, int BN, int WM, int WN>
+struct Tile {
+  static constexpr int NWAVES = WM * WN;
+  static constexpr int NTHREADS = NWAVES * 64;
+  static constexpr int WTM = BM / WM;  // rows of a per wave
+  static constexpr int WTN = BN / WN;  // rows of b (output columns) per wave
+  static constexpr int IG = WTM / 16;
+  static constexpr int JG = WTN / 16;
+  static constexpr int A_BYTES = BM * KBLK;
+  static constexpr int B_BYTES = BN * KBLK;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int A_LOADS = BM / SLAB_ROWS / NWAVES;  // per wave and K block
+  static constexpr int B_LOADS = BN / SLAB_ROWS / NWAVES;
+  static_assert(BM % (SLAB_ROWS * NWAVES) == 0 && BN % (SLAB_ROWS * NWAVES) == 0, "slabs");
+  static_assert(WTM % 16 == 0 && WTN % 16 == 0, "16x16 MFMA blocks");
+  static_assert(128 % WTN == 0, "a wave's columns must sit in one 128-wide b-scale block");
+};
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4). The LDS
+// address is wave-uniform: lane l writes bytes [16l, 16l+16) of the 1 KB block at `lds`.
+__device__ __forceinline__ void load_lds_16(const uint8_t* gsrc, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(const_cast<uint8_t*>(gsrc), lds, 16, 0, 0);
+}
+
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Renumber workgroups so that ids t and t+1 run on the same XCD (dispatch is round-robin).
+__device__ __forceinline__ int xcd_local_order(int t, int total) {
+  const int full = total & ~7;
+  return t < full ? (t & 7) * (full >> 3) + (t >> 3) : t;
+}
+
+__device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int group_m, int& tm, int& tn) {
+  const int per_group = group_m * tiles_n;
+  const int gid = t / per_group;
+  const int first = gid * group_m;
+  const int gm = min(tiles_m - first, group_m);
+  const int r = t - gid * per_group;
+  tm = first + r % gm;
+  tn = r / gm;
+}
+
+// One 16x128 FP8 operand fragment: lane l supplies row (l & 15) of the 16-row group and the 32
+// bytes at K offset 32*(l >> 4) of the K block. Both operands use the same K assignment, which is
+// all the matrix core needs for a dot product over the block.
+__device__ __forceinline__ i32x8 load_frag(const uint8_t* slab, int row, int lane) {
+  const uint8_t* rp = slab + row * KBLK;
+  const int c0 = (lane >> 4) * 2;
+  const int sw = row & 7;
+  const i32x4 lo = *reinterpret_cast<const i32x4*>(rp + ((c0 ^ sw) << 4));
+  const i32x4 hi = *reinterpret_cast<const i32x4*>(rp + (((c0 + 1) ^ sw) << 4));
+  return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+}
+
+template <int BM, int BN, int WM, int WN, int MODE>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_fp8_groupwise_kernel(const GemmParams p) {
+  using T = Tile<BM, BN, WM, WN>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::STAGE_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+
+  // ---- tile scheduling ---------------------------------------------------------------------
+  int t = xcd_local_order(blockIdx.x, gridDim.x);
+  int g = 0;
+  if (MODE == MODE_MASKED) {
+    const int per = p.tiles_m * p.tiles_n;
+    g = t / per;
+    t -= g * per;
+  }
+  int tm, tn;
+  raster(t, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+  const int row0 = tm * BM;
+  const int col0 = tn * BN;
+
+  int row_end = p.m;  // rows at or beyond row_end hold no valid output
+  int bsel = 0;       // group of b / b_scale
+  if (MODE == MODE_MASKED) {
+    const int mm = max(0, min(p.rowinfo[g], p.m));
+    if (row0 >= mm) return;
+    row_end = mm;
+    bsel = g;
+  } else if (MODE == MODE_CONTIG) {
+    int e = -1;
+    for (int r = lane; r < BM; r += 64) e = max(e, p.rowinfo[row0 + r]);
+    e = wave_max(e);
+    if (e < 0 || e >= p.num_groups) return;  // padding-only tile
+    bsel = e;
+  }
+
+  const uint8_t* A = p.a + (int64_t)g * p.a_group_stride;
+  const uint8_t* B = p.b + (int64_t)bsel * p.b_group_stride;
+  const float* SA = p.sa + (int64_t)g * p.sa_group_stride;
+  const float* SB = p.sb + (int64_t)bsel * p.sb_group_stride;
+
+  // ---- HBM -> LDS load assignment ----------------------------------------------------------
+  // Slab s (1 KB) holds tile rows [8s, 8s+8); lane l fills its chunk l, i.e. row 8s + (l>>3),
+  // physical chunk (l & 7), which holds logical chunk (l & 7) ^ (l >> 3).
+  const int lrow = lane >> 3;
+  const int lchunk = (lane & 7) ^ lrow;
+  uint32_t a_off[T::A_LOADS], b_off[T::B_LOADS];
+  bool a_live[T::A_LOADS], b_live[T::B_LOADS];
+#pragma unroll
+  for (int q = 0; q < T::A_LOADS; ++q) {
+    const int slab_row = (wave * T::A_LOADS + q) * SLAB_ROWS;
+    const int r = min(row0 + slab_row + lrow, p.m - 1);
+    a_off[q] = (uint32_t)r * (uint32_t)p.k + lchunk * 16;
+    a_live[q] = row0 + slab_row < row_end;
+  }
+#pragma unroll
+  for (int q = 0; q < T::B_LOADS; ++q) {
+    const int slab_row = (wave * T::B_LOADS + q) * SLAB_ROWS;
+    const int r = min(col0 + slab_row + lrow, p.n - 1);
+    b_off[q] = (uint32_t)r * (uint32_t)p.k + lchunk * 16;
+    b_live[q] = col0 + slab_row < p.n;
+  }
+
+  // ---- this wave's output block and scale addressing -----------------------------------------
+  const int i0 = (wave % WM) * T::WTM;
+  const int j0 = (wave / WM) * T::WTN;
+  const bool wave_live = (row0 + i0 < row_end) && (col0 + j0 < p.n);
+  const int fr = lane & 15;
+  int sa_off[T::IG];
+#pragma unroll
+  for (int ig = 0; ig < T::IG; ++ig) {
+    const int r = min(row0 + i0 + ig * 16 + fr, p.m - 1);
+    sa_off[ig] = r * p.sa_row_stride;
+  }
+  const int nb = min((col0 + j0) / 128, p.nblocks - 1);
+  const int sb_off = nb * p.sb_nb_stride;
+
+  f32x4 acc[T::IG][T::JG];
+#pragma unroll
+  for (int ig = 0; ig < T::IG; ++ig)
+#pragma unroll
+    for (int jg = 0; jg < T::JG; ++jg) acc[ig][jg] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto issue_loads = [&](int kb, int stage) {
+    uint8_t* sA = smem + stage * T::STAGE_BYTES;
+    uint8_t* sB = sA + T::A_BYTES;
+    const uint32_t koff = (uint32_t)kb * KBLK;
+#pragma unroll
+    for (int q = 0; q < T::A_LOADS; ++q)
+      if (a_live[q])
+        load_lds_16(A + a_off[q] + koff, sA + (wave * T::A_LOADS + q) * 1024);
+#pragma unroll
+    for (int q = 0; q < T::B_LOADS; ++q)
+      if (b_live[q])
+        load_lds_16(B + b_off[q] + koff, sB + (wave * T::B_LOADS + q) * 1024);
+  };
+
+  float sa_next[T::IG];
+  float sb_next = 0.f;
+  auto load_scales = [&](int kb) {
+#pragma unroll
+    for (int ig = 0; ig < T::IG; ++ig) sa_next[ig] = SA[sa_off[ig] + kb * p.sa_kb_stride];
+    sb_next = SB[sb_off + kb * p.sb_kb_stride];
+  };
+
+  const int KB = p.kblocks;
+  if (KB > 0) {
+    issue_loads(0, 0);
+    load_scales(0);
+  }
+  wait_vmem();
+  __syncthreads();
+
+  for (int kb = 0; kb < KB; ++kb) {
+    const int stage = kb & 1;
+    float s[T::IG];
+#pragma unroll
+    for (int ig = 0; ig < T::IG; ++ig) s[ig] = sa_next[ig] * sb_next;
+    if (kb + 1 < KB) {
+      issue_loads(kb + 1, stage ^ 1);
+      load_scales(kb + 1);
+    }
+    if (wave_live) {
+      const uint8_t* sA = smem + stage * T::STAGE_BYTES;
+      const uint8_t* sB = sA + T::A_BYTES;
+      i32x8 af[T::IG];
+#pragma unroll
+      for (int ig = 0; ig < T::IG; ++ig) af[ig] = load_frag(sA, i0 + ig * 16 + fr, lane);
+#pragma unroll
+      for (int jg = 0; jg < T::JG; ++jg) {
+        const i32x8 bfr = load_frag(sB, j0 + jg * 16 + fr, lane);
+#pragma unroll
+        for (int ig = 0; ig < T::IG; ++ig) {
+          const f32x4 pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              bfr, af[ig], f32x4{0.f, 0.f, 0.f, 0.f}, FMT_E4M3, FMT_E4M3, 0, E8M0_ONE, 0, E8M0_ONE);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[ig][jg][r] = __builtin_fmaf(pr[r], s[ig], acc[ig][jg][r]);
+        }
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // ---- epilogue: BF16 round-to-nearest-even, 8-byte stores of valid rows ---------------------
+  if (!wave_live) return;
+  uint16_t* O = p.out + (int64_t)g * p.out_group_stride;
+  const int jl = (lane >> 4) * 4;
+#pragma unroll
+  for (int ig = 0; ig < T::IG; ++ig) {
+    const int i = row0 + i0 + ig * 16 + fr;
+    bool ok = i < row_end;
+    if (MODE == MODE_CONTIG) ok = ok && p.rowinfo[i] == bsel;
+    if (!ok) continue;
+    uint16_t* orow = O + (int64_t)i * p.n;
+#pragma unroll
+    for (int jg = 0; jg < T::JG; ++jg) {
+      const int j = col0 + j0 + jg * 16 + jl;
+      if (j >= p.n) continue;
+      const bf16x2 lo = {(__bf16)acc[ig][jg][0], (__bf16)acc[ig][jg][1]};
+      const bf16x2 hi = {(__bf16)acc[ig][jg][2], (__bf16)acc[ig][jg][3]};
+      uint2 v;
+      v.x = __builtin_bit_cast(uint32_t, lo);
+      v.y = __builtin_bit_cast(uint32_t, hi);
+      *reinterpret_cast<uint2*>(orow + j) = v;
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_cfg(GemmMode mode, const GemmParams& p, int grid, hipStream_t stream) {
+  const dim3 block(WM * WN * 64);
+  switch (mode) {
+    case MODE_PLAIN:
+      hipLaunchKernelGGL((gemm_fp8_groupwise_kernel<BM, BN, WM, WN, MODE_PLAIN>), dim3(grid), block, 0, stream, p);
+      break;
+    case MODE_CONTIG:
+      hipLaunchKernelGGL((gemm_fp8_groupwise_kernel<BM, BN, WM, WN, MODE_CONTIG>), dim3(grid), block, 0, stream, p);
+      break;
+    case MODE_MASKED:
+      hipLaunchKernelGGL((gemm_fp8_groupwise_kernel<BM, BN, WM, WN, MODE_MASKED>), dim3(grid), block, 0, stream, p);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kernels
+
+using namespace kernels;
+
+int tile_rows(TileConfig cfg) { return cfg == TILE_256x256 ? 256 : 128; }
+int tile_cols(TileConfig cfg) { return 256; }
+
+hipError_t launch_gemm(GemmMode mode, TileConfig cfg, GemmParams p, int grid, hipStream_t stream) {
+  if (cfg == TILE_256x256) return launch_cfg<256, 256, 4, 2>(mode, p, grid, stream);
+  return launch_cfg<128, 256, 2, 4>(mode, p, grid, stream);
+}
+
+}  // namespace fp8g

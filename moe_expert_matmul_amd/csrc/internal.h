@@ -1,0 +1,59 @@
+// Internal interface between the C-ABI layer (api.hip) and the kernel files (gemm.hip, moe.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8g {
+
+// Which tile scheduler the GEMM kernel runs.
+enum GemmMode : int {
+  MODE_PLAIN = 0,   // out = a @ b.T
+  MODE_CONTIG = 1,  // per 128-row tile, b chosen by the tile's expert in m_indices
+  MODE_MASKED = 2,  // per group g, rows below masked_m[g]
+};
+
+// Everything the GEMM kernel needs, passed by value as the kernel argument. Strides in elements.
+struct GemmParams {
+  const uint8_t* a;
+  const uint8_t* b;
+  const float* sa;
+  const float* sb;
+  uint16_t* out;
+  const int32_t* rowinfo;  // m_indices (CONTIG) or masked_m (MASKED)
+  int64_t a_group_stride, b_group_stride, sa_group_stride, sb_group_stride, out_group_stride;
+  int32_t m;  // PLAIN/CONTIG: rows of a; MASKED: max_m
+  int32_t n, k;
+  int32_t kblocks, nblocks;
+  int32_t sa_row_stride, sa_kb_stride;  // a_scale element of (row, kb)
+  int32_t sb_nb_stride, sb_kb_stride;   // b_scale element of (n block, kb)
+  int32_t num_groups;
+  int32_t tiles_m, tiles_n, group_m;
+};
+
+// Tile configurations the host may pick. Results are identical for every configuration.
+enum TileConfig : int {
+  TILE_256x256 = 0,  // 8 waves as 4 (rows) x 2 (cols), 64x128 per wave
+  TILE_128x256 = 1,  // 8 waves as 2 x 4, 64x64 per wave
+};
+
+int tile_rows(TileConfig cfg);
+int tile_cols(TileConfig cfg);
+
+hipError_t launch_gemm(GemmMode mode, TileConfig cfg, GemmParams p, int grid, hipStream_t stream);
+
+hipError_t launch_moe_build_permutation(const int32_t* topk_ids, int num_tokens, int top_k,
+                                        int num_experts, int m_alloc, int32_t* m_indices,
+                                        int32_t* src_token, int32_t* row_of_entry,
+                                        hipStream_t stream);
+hipError_t launch_moe_gather_quant(const uint16_t* x, const int32_t* src_token, int num_tokens,
+                                   int hidden, int m_alloc, uint8_t* a_out, float* a_scale_out,
+                                   hipStream_t stream);
+hipError_t launch_moe_silu_mul_quant(const uint16_t* y, const int32_t* m_indices, int rows,
+                                     int inter, uint8_t* a_out, float* a_scale_out,
+                                     hipStream_t stream);
+hipError_t launch_moe_combine(const uint16_t* y, const int32_t* row_of_entry,
+                              const float* topk_weights, int num_tokens, int top_k, int hidden,
+                              int m_alloc, uint16_t* out, hipStream_t stream);
+
+}  // namespace fp8g

@@ -1,0 +1,173 @@
+"""Python binding of the three groupwise FP8 GEMM entry points (argument marshalling only).
+
+The ``fp8_*`` functions mirror the C ABI (include/fp8g.h) one to one and write into a caller-given
+``out``. The ``gemm_fp8_nt_groupwise`` / ``group_deepgemm_fp8_nt_groupwise`` /
+``batch_deepgemm_fp8_nt_groupwise`` wrappers follow the parameter lists of the MATE FlashInfer-API
+page (section "GEMM"): they allocate ``out`` when it is omitted and return it. PyTorch supplies
+device memory and the current stream; every step of the computation runs in libfp8g.so.
+"""
+
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+_FP8_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+_GRAN = (1, 128, 128)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(t: torch.Tensor, name: str, dtypes, shape, device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _major(scale_major) -> int:
+    if scale_major in (None, "K", _lib.SCALE_K_MAJOR):
+        return _lib.SCALE_K_MAJOR
+    if scale_major in ("MN", _lib.SCALE_MN_MAJOR):
+        return _lib.SCALE_MN_MAJOR
+    raise ValueError(f"scale_major must be 'K' or 'MN', got {scale_major!r}")
+
+
+def _require_cuda(a: torch.Tensor) -> torch.device:
+    if not isinstance(a, torch.Tensor) or a.device.type != "cuda":
+        raise ValueError("operands must be HIP device tensors (device 'cuda')")
+    return a.device
+
+
+def fp8_gemm_nt_groupwise(a, b, a_scale, b_scale, out, scale_major="K", granularity=_GRAN) -> torch.Tensor:
+    """out (m,n) bf16 = a (m,k) @ b (n,k).T with 1x128 / 128x128 FP32 scales."""
+    dev = _require_cuda(a)
+    m, k = a.shape
+    n = b.shape[0]
+    kb, nb = k // 128, n // 128
+    major = _major(scale_major)
+    _check(a, "a", _FP8_DTYPES, (m, k), dev)
+    _check(b, "b", _FP8_DTYPES, (n, k), dev)
+    _check(a_scale, "a_scale", (torch.float32,), (m, kb) if major == 0 else (kb, m), dev)
+    _check(b_scale, "b_scale", (torch.float32,), (nb, kb) if major == 0 else (kb, nb), dev)
+    _check(out, "out", (torch.bfloat16,), (m, n), dev)
+    with torch.cuda.device(dev):
+        st = _lib.load().fp8_gemm_nt_groupwise(_ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale), _ptr(out),
+                                               m, n, k, major, *granularity, _stream(dev))
+    _lib.check(st, "fp8_gemm_nt_groupwise")
+    return out
+
+
+def fp8_group_gemm_contiguous(a, b, a_scale, b_scale, m_indices, out, scale_major="K",
+                              granularity=_GRAN) -> torch.Tensor:
+    """out[i] = a[i] @ b[m_indices[i]].T for rows with m_indices[i] >= 0 (others untouched)."""
+    dev = _require_cuda(a)
+    m, k = a.shape
+    groups, n, _ = b.shape
+    kb, nb = k // 128, n // 128
+    major = _major(scale_major)
+    _check(a, "a", _FP8_DTYPES, (m, k), dev)
+    _check(b, "b", _FP8_DTYPES, (groups, n, k), dev)
+    _check(a_scale, "a_scale", (torch.float32,), (m, kb) if major == 0 else (kb, m), dev)
+    _check(b_scale, "b_scale", (torch.float32,), (groups, nb, kb) if major == 0 else (groups, kb, nb), dev)
+    _check(m_indices, "m_indices", (torch.int32,), (m,), dev)
+    _check(out, "out", (torch.bfloat16,), (m, n), dev)
+    with torch.cuda.device(dev):
+        st = _lib.load().fp8_group_gemm_contiguous(_ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale), _ptr(m_indices),
+                                                   _ptr(out), m, n, k, groups, major, *granularity, _stream(dev))
+    _lib.check(st, "fp8_group_gemm_contiguous")
+    return out
+
+
+def fp8_batch_gemm_masked(a, b, a_scale, b_scale, masked_m, expected_m, out, scale_major="K",
+                          granularity=_GRAN) -> torch.Tensor:
+    """out[g, :masked_m[g]] = a[g, :masked_m[g]] @ b[g].T (other rows untouched)."""
+    dev = _require_cuda(a)
+    groups, max_m, k = a.shape
+    n = b.shape[1]
+    kb, nb = k // 128, n // 128
+    major = _major(scale_major)
+    _check(a, "a", _FP8_DTYPES, (groups, max_m, k), dev)
+    _check(b, "b", _FP8_DTYPES, (groups, n, k), dev)
+    _check(a_scale, "a_scale", (torch.float32,), (groups, max_m, kb) if major == 0 else (groups, kb, max_m), dev)
+    _check(b_scale, "b_scale", (torch.float32,), (groups, nb, kb) if major == 0 else (groups, kb, nb), dev)
+    _check(masked_m, "masked_m", (torch.int32,), (groups,), dev)
+    _check(out, "out", (torch.bfloat16,), (groups, max_m, n), dev)
+    with torch.cuda.device(dev):
+        st = _lib.load().fp8_batch_gemm_masked(_ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale), _ptr(masked_m),
+                                               int(expected_m), _ptr(out), groups, max_m, n, k, major,
+                                               *granularity, _stream(dev))
+    _lib.check(st, "fp8_batch_gemm_masked")
+    return out
+
+
+def _out_dtype(out, out_dtype):
+    if out is not None:
+        return out.dtype
+    if out_dtype not in (None, torch.bfloat16):
+        raise NotImplementedError("only BF16 output is implemented")
+    return torch.bfloat16
+
+
+def gemm_fp8_nt_groupwise(a: torch.Tensor, b: torch.Tensor, a_scale: torch.Tensor, b_scale: torch.Tensor,
+                          scale_major_mode: Optional[str] = None, mma_sm: int = 1,
+                          scale_granularity_mnk: Tuple[int, int, int] = _GRAN, out: Optional[torch.Tensor] = None,
+                          out_dtype: Optional[torch.dtype] = None, backend: str = "auto",
+                          output_scale: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Groupwise FP8 NT GEMM with the MATE page's parameters; ``mma_sm`` has no meaning here and is
+    ignored, ``backend`` must be 'auto', FP8 output (``output_scale``) is not implemented. A 0-d
+    ``b_scale`` is one scale for every 128x128 block of b."""
+    if backend != "auto":
+        raise NotImplementedError("backend must be 'auto'")
+    if output_scale is not None:
+        raise NotImplementedError("FP8 output (output_scale) is not implemented")
+    _out_dtype(out, out_dtype)
+    m, k = a.shape
+    n = b.shape[0]
+    major = _major(scale_major_mode)
+    if b_scale.dim() == 0:
+        shape = (n // 128, k // 128) if major == 0 else (k // 128, n // 128)
+        b_scale = b_scale.to(torch.float32).expand(shape).contiguous()
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    return fp8_gemm_nt_groupwise(a, b, a_scale, b_scale, out, major, tuple(scale_granularity_mnk))
+
+
+def group_deepgemm_fp8_nt_groupwise(a: torch.Tensor, b: torch.Tensor, a_scale: torch.Tensor,
+                                    b_scale: torch.Tensor, m_indices: torch.Tensor,
+                                    scale_granularity_mnk: Tuple[int, int, int] = _GRAN,
+                                    out: Optional[torch.Tensor] = None,
+                                    out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    """Contiguous grouped FP8 NT GEMM (K-major scales); padding rows of ``out`` are unspecified."""
+    if out is None:
+        _out_dtype(None, out_dtype)
+        out = torch.empty((a.shape[0], b.shape[1]), dtype=torch.bfloat16, device=a.device)
+    return fp8_group_gemm_contiguous(a, b, a_scale, b_scale, m_indices, out, "K", tuple(scale_granularity_mnk))
+
+
+def batch_deepgemm_fp8_nt_groupwise(a: torch.Tensor, b: torch.Tensor, a_scale: torch.Tensor,
+                                    b_scale: torch.Tensor, masked_m: torch.Tensor, expected_m: int,
+                                    scale_granularity_mnk: Tuple[int, int, int] = _GRAN,
+                                    out: Optional[torch.Tensor] = None,
+                                    out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    """Masked batched FP8 NT GEMM (K-major scales); rows at or beyond masked_m[g] are unspecified."""
+    if out is None:
+        _out_dtype(None, out_dtype)
+        out = torch.empty((a.shape[0], a.shape[1], b.shape[1]), dtype=torch.bfloat16, device=a.device)
+    return fp8_batch_gemm_masked(a, b, a_scale, b_scale, masked_m, expected_m, out, "K",
+                                 tuple(scale_granularity_mnk))

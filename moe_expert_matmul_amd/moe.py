@@ -1,0 +1,137 @@
+"""FP8 block-scale expert FFN on the contiguous grouped GEMM (argument marshalling only).
+
+Follows the DeepSeek FP8 block-scale mode of the flashinfer-rs README (section "API Example: Fused
+MoE FP8 (cudarc)"): BF16 tokens, int32 top-k expert ids, FP8 fc1 weights (E, 2*inter, hidden) whose
+first ``inter`` rows are the gate and the next ``inter`` the up projection, FP8 fc2 weights
+(E, hidden, inter), 128x128 FP32 block scales, and the top-k routing weights for the combine.
+
+Six library calls on the current stream, no host synchronisation:
+  permutation -> gather+quantise -> fc1 grouped GEMM -> SiLU-mul+quantise -> fc2 grouped GEMM -> combine
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from .gemm import _check, _require_cuda, _stream, fp8_group_gemm_contiguous
+
+
+def default_m_alloc(num_tokens: int, top_k: int, num_experts: int) -> int:
+    """Rows that hold every expert region for any routing (each region is padded to 128 rows)."""
+    worst = num_tokens * top_k + num_experts * 127
+    return (worst + 127) // 128 * 128
+
+
+@dataclass
+class MoeWorkspace:
+    """Device buffers of one expert-FFN call (allocated once, reused across calls)."""
+
+    m_indices: torch.Tensor
+    src_token: torch.Tensor
+    row_of_entry: torch.Tensor
+    a1: torch.Tensor
+    sa1: torch.Tensor
+    y1: torch.Tensor
+    a2: torch.Tensor
+    sa2: torch.Tensor
+    y2: torch.Tensor
+
+    @staticmethod
+    def allocate(num_tokens, top_k, num_experts, hidden, inter, device) -> "MoeWorkspace":
+        m_alloc = default_m_alloc(num_tokens, top_k, num_experts)
+        e = dict(device=device)
+        return MoeWorkspace(
+            m_indices=torch.empty(m_alloc, dtype=torch.int32, **e),
+            src_token=torch.empty(m_alloc, dtype=torch.int32, **e),
+            row_of_entry=torch.empty((num_tokens, top_k), dtype=torch.int32, **e),
+            a1=torch.empty((m_alloc, hidden), dtype=torch.uint8, **e),
+            sa1=torch.empty((m_alloc, hidden // 128), dtype=torch.float32, **e),
+            y1=torch.empty((m_alloc, 2 * inter), dtype=torch.bfloat16, **e),
+            a2=torch.empty((m_alloc, inter), dtype=torch.uint8, **e),
+            sa2=torch.empty((m_alloc, inter // 128), dtype=torch.float32, **e),
+            y2=torch.empty((m_alloc, hidden), dtype=torch.bfloat16, **e),
+        )
+
+    @property
+    def m_alloc(self) -> int:
+        return self.m_indices.shape[0]
+
+
+def moe_build_permutation(topk_ids, num_experts, m_indices, src_token, row_of_entry):
+    dev = _require_cuda(topk_ids)
+    t, k = topk_ids.shape
+    m_alloc = m_indices.shape[0]
+    _check(topk_ids, "topk_ids", (torch.int32,), (t, k), dev)
+    _check(m_indices, "m_indices", (torch.int32,), (m_alloc,), dev)
+    _check(src_token, "src_token", (torch.int32,), (m_alloc,), dev)
+    _check(row_of_entry, "row_of_entry", (torch.int32,), (t, k), dev)
+    with torch.cuda.device(dev):
+        st = _lib.load().fp8_moe_build_permutation(topk_ids.data_ptr(), t, k, num_experts, m_alloc,
+                                                   m_indices.data_ptr(), src_token.data_ptr(),
+                                                   row_of_entry.data_ptr(), _stream(dev))
+    _lib.check(st, "fp8_moe_build_permutation")
+
+
+def moe_gather_quant(x, src_token, a_out, a_scale_out):
+    dev = _require_cuda(x)
+    t, h = x.shape
+    m_alloc = src_token.shape[0]
+    _check(x, "x", (torch.bfloat16,), (t, h), dev)
+    _check(src_token, "src_token", (torch.int32,), (m_alloc,), dev)
+    _check(a_out, "a_out", (torch.uint8, torch.float8_e4m3fn), (m_alloc, h), dev)
+    _check(a_scale_out, "a_scale_out", (torch.float32,), (m_alloc, h // 128), dev)
+    with torch.cuda.device(dev):
+        st = _lib.load().fp8_moe_gather_quant(x.data_ptr(), src_token.data_ptr(), t, h, m_alloc,
+                                              a_out.data_ptr(), a_scale_out.data_ptr(), _stream(dev))
+    _lib.check(st, "fp8_moe_gather_quant")
+
+
+def moe_silu_mul_quant(y, m_indices, a_out, a_scale_out):
+    dev = _require_cuda(y)
+    rows, two_i = y.shape
+    inter = two_i // 2
+    _check(y, "y", (torch.bfloat16,), (rows, 2 * inter), dev)
+    _check(m_indices, "m_indices", (torch.int32,), (rows,), dev)
+    _check(a_out, "a_out", (torch.uint8, torch.float8_e4m3fn), (rows, inter), dev)
+    _check(a_scale_out, "a_scale_out", (torch.float32,), (rows, inter // 128), dev)
+    with torch.cuda.device(dev):
+        st = _lib.load().fp8_moe_silu_mul_quant(y.data_ptr(), m_indices.data_ptr(), rows, inter,
+                                                a_out.data_ptr(), a_scale_out.data_ptr(), _stream(dev))
+    _lib.check(st, "fp8_moe_silu_mul_quant")
+
+
+def moe_combine(y, row_of_entry, topk_weights, out):
+    dev = _require_cuda(y)
+    m_alloc, h = y.shape
+    t, k = row_of_entry.shape
+    _check(y, "y", (torch.bfloat16,), (m_alloc, h), dev)
+    _check(row_of_entry, "row_of_entry", (torch.int32,), (t, k), dev)
+    _check(topk_weights, "topk_weights", (torch.float32,), (t, k), dev)
+    _check(out, "out", (torch.bfloat16,), (t, h), dev)
+    with torch.cuda.device(dev):
+        st = _lib.load().fp8_moe_combine(y.data_ptr(), row_of_entry.data_ptr(), topk_weights.data_ptr(), t, k, h,
+                                         m_alloc, out.data_ptr(), _stream(dev))
+    _lib.check(st, "fp8_moe_combine")
+
+
+def moe_ffn_fp8_block_scale(x, topk_ids, topk_weights, w1, s1, w2, s2, out=None, workspace=None):
+    """Expert FFN: out (T, hidden) bf16. ``workspace`` (MoeWorkspace) keeps every intermediate."""
+    num_tokens, hidden = x.shape
+    num_experts, two_inter, _ = w1.shape
+    inter = two_inter // 2
+    top_k = topk_ids.shape[1]
+    if w2.shape != (num_experts, hidden, inter):
+        raise ValueError(f"w2 has shape {tuple(w2.shape)}, expected {(num_experts, hidden, inter)}")
+    ws = workspace or MoeWorkspace.allocate(num_tokens, top_k, num_experts, hidden, inter, x.device)
+    if out is None:
+        out = torch.empty((num_tokens, hidden), dtype=torch.bfloat16, device=x.device)
+    moe_build_permutation(topk_ids, num_experts, ws.m_indices, ws.src_token, ws.row_of_entry)
+    moe_gather_quant(x, ws.src_token, ws.a1, ws.sa1)
+    fp8_group_gemm_contiguous(ws.a1, w1, ws.sa1, s1, ws.m_indices, ws.y1)
+    moe_silu_mul_quant(ws.y1, ws.m_indices, ws.a2, ws.sa2)
+    fp8_group_gemm_contiguous(ws.a2, w2, ws.sa2, s2, ws.m_indices, ws.y2)
+    moe_combine(ws.y2, ws.row_of_entry, topk_weights, out)
+    return out

@@ -1,0 +1,130 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point the header declares,
+and rejects bad arguments on the host before touching a device."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from moe_expert_matmul_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8g.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return set(re.findall(r"FP8G_API\s+[\w\s\*]+?\b(\w+)\s*\(", text))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libfp8g.so is not built (run `python -m moe_expert_matmul_amd.build`)")
+    return _lib.load()
+
+
+def test_header_declares_the_three_gemm_forms_and_the_moe_steps():
+    names = _declared()
+    assert {"fp8_gemm_nt_groupwise", "fp8_group_gemm_contiguous", "fp8_batch_gemm_masked",
+            "fp8g_last_error", "fp8_moe_build_permutation", "fp8_moe_gather_quant",
+            "fp8_moe_silu_mul_quant", "fp8_moe_combine"} <= names
+    assert names == set(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert exported == _declared(), exported ^ _declared()
+
+
+def test_version(lib):
+    assert lib.fp8g_version() >= 100
+
+
+GRAN = (1, 128, 128)
+P = ctypes.c_void_p(16)  # a non-null, 16-byte aligned dummy (never dereferenced: validation fails first)
+
+
+def _status(fn, *args):
+    st = fn(*args)
+    return st, _lib.load().fp8g_last_error().decode()
+
+
+def test_plain_rejects_k_not_multiple_of_128(lib):
+    st, msg = _status(lib.fp8_gemm_nt_groupwise, P, P, P, P, P, 4, 128, 100, 0, *GRAN, None)
+    assert st == _lib.INVALID_ARGUMENT and "k (100)" in msg
+
+
+def test_plain_rejects_n_not_multiple_of_128(lib):
+    st, msg = _status(lib.fp8_gemm_nt_groupwise, P, P, P, P, P, 4, 200, 128, 0, *GRAN, None)
+    assert st == _lib.INVALID_ARGUMENT and "n (200)" in msg
+
+
+def test_plain_rejects_negative_sizes_and_bad_layout(lib):
+    assert lib.fp8_gemm_nt_groupwise(P, P, P, P, P, -1, 128, 128, 0, *GRAN, None) == _lib.INVALID_ARGUMENT
+    st, msg = _status(lib.fp8_gemm_nt_groupwise, P, P, P, P, P, 4, 128, 128, 7, *GRAN, None)
+    assert st == _lib.INVALID_ARGUMENT and "scale_major" in msg
+
+
+def test_unsupported_granularity_is_not_supported(lib):
+    st, msg = _status(lib.fp8_gemm_nt_groupwise, P, P, P, P, P, 4, 128, 128, 0, 1, 64, 128, None)
+    assert st == _lib.NOT_SUPPORTED and "granularity" in msg
+    st, _ = _status(lib.fp8_group_gemm_contiguous, P, P, P, P, P, P, 128, 128, 128, 2, 0, 128, 128, 128, None)
+    assert st == _lib.NOT_SUPPORTED
+
+
+def test_null_and_misaligned_pointers_are_rejected(lib):
+    st, msg = _status(lib.fp8_gemm_nt_groupwise, None, P, P, P, P, 4, 128, 128, 0, *GRAN, None)
+    assert st == _lib.INVALID_ARGUMENT and "non-null" in msg
+    st, msg = _status(lib.fp8_gemm_nt_groupwise, ctypes.c_void_p(17), P, P, P, P, 4, 128, 128, 0, *GRAN, None)
+    assert st == _lib.INVALID_ARGUMENT and "aligned" in msg
+
+
+def test_empty_problems_are_successful_no_ops(lib):
+    assert lib.fp8_gemm_nt_groupwise(None, None, None, None, None, 0, 128, 128, 0, *GRAN, None) == _lib.OK
+    assert lib.fp8_gemm_nt_groupwise(None, None, None, None, None, 5, 0, 128, 0, *GRAN, None) == _lib.OK
+    assert lib.fp8_batch_gemm_masked(None, None, None, None, None, 0, None, 0, 64, 128, 128, 0, *GRAN, None) == _lib.OK
+    assert lib.fp8_group_gemm_contiguous(None, None, None, None, None, None, 0, 128, 128, 4, 0, *GRAN, None) == _lib.OK
+    assert lib.fp8g_last_error() == b""
+
+
+def test_contiguous_requires_128_row_multiple(lib):
+    st, msg = _status(lib.fp8_group_gemm_contiguous, P, P, P, P, P, P, 100, 128, 128, 2, 0, *GRAN, None)
+    assert st == _lib.INVALID_ARGUMENT and "multiple of 128" in msg
+
+
+def test_masked_rejects_negative_expected_m(lib):
+    st, _ = _status(lib.fp8_batch_gemm_masked, P, P, P, P, P, -1, P, 2, 64, 128, 128, 0, *GRAN, None)
+    assert st == _lib.INVALID_ARGUMENT
+
+
+def test_moe_steps_validate_sizes(lib):
+    # m_alloc too small for 4 tokens x 2 slots over 3 experts (needs 128 * ceil((8 + 381) / 128) = 512)
+    st, msg = _status(lib.fp8_moe_build_permutation, P, 4, 2, 3, 256, P, P, P, None)
+    assert st == _lib.INVALID_ARGUMENT and "m_alloc" in msg
+    st, _ = _status(lib.fp8_moe_gather_quant, P, P, 4, 100, 128, P, P, None)
+    assert st == _lib.INVALID_ARGUMENT
+    st, _ = _status(lib.fp8_moe_silu_mul_quant, P, P, 128, 100, P, P, None)
+    assert st == _lib.INVALID_ARGUMENT
+    st, _ = _status(lib.fp8_moe_combine, P, P, P, 4, 65, 128, 128, P, None)
+    assert st == _lib.INVALID_ARGUMENT
+
+
+def test_error_message_is_cleared_by_the_next_successful_call(lib):
+    lib.fp8_gemm_nt_groupwise(P, P, P, P, P, 4, 128, 100, 0, *GRAN, None)
+    assert lib.fp8g_last_error() != b""
+    assert lib.fp8_gemm_nt_groupwise(None, None, None, None, None, 0, 128, 128, 0, *GRAN, None) == _lib.OK
+    assert lib.fp8g_last_error() == b""
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    from moe_expert_matmul_amd import gemm_fp8_nt_groupwise
+    a = torch.zeros((4, 128), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        gemm_fp8_nt_groupwise(a, a, torch.ones(4, 1), torch.ones(1, 1))

@@ -1,0 +1,312 @@
+"""GPU parity of the three groupwise FP8 GEMM forms against the float64 oracle (MI355X only).
+
+Every case prints its name before it touches the GPU. Small cases compare every output element;
+the full workload sizes (4096x4096x7168 plain, 32 Zipf-sized experts, 16 masked groups) compare
+sampled rows and column blocks, computed by the oracle one sample at a time.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_matmul_amd as fp8g
+import workloads
+from oracle import bf16, gemm as ogemm
+from parity import assert_within_tolerance, bf16_values, host, say, sentinel_like, untouched
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _plain_call(d, major="K", out=None):
+    a, b, sa, sb = d["a"], d["b"], d["a_scale"], d["b_scale"]
+    if major == "MN":
+        sa, sb = sa.t().contiguous(), sb.t().contiguous()
+    if out is None:
+        out = sentinel_like((a.shape[0], b.shape[0]), DEV)
+    fp8g.fp8_gemm_nt_groupwise(a, b, sa, sb, out, major)
+    torch.cuda.synchronize()
+    return out
+
+
+def _plain_ref(d, rows=None):
+    a, sa = host(d["a"]), host(d["a_scale"])
+    if rows is not None:
+        a, sa = a[rows], sa[rows]
+    return ogemm.gemm_fp8_nt_groupwise(a, host(d["b"]), sa, host(d["b_scale"]))
+
+
+PLAIN_SHAPES = [(128, 256, 512), (1, 128, 128), (17, 128, 256), (129, 384, 256), (300, 640, 1024),
+                (513, 768, 384), (1000, 1152, 640), (256, 256, 128)]
+
+
+@pytest.mark.parametrize("m,n,k", PLAIN_SHAPES)
+def test_plain_matches_oracle(m, n, k):
+    say("plain", m, n, k)
+    d = workloads.plain(m, n, k, seed=m + n + k, device=DEV)
+    out = _plain_call(d)
+    assert_within_tolerance(bf16_values(out), _plain_ref(d), f"plain {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(300, 640, 1024), (4096, 512, 256)])
+def test_mn_major_scales_give_bitwise_identical_output(m, n, k):
+    say("plain K vs MN major", m, n, k)
+    d = workloads.plain(m, n, k, seed=7, device=DEV)
+    k_out = host(_plain_call(d, "K"))
+    mn_out = host(_plain_call(d, "MN"))
+    assert np.array_equal(k_out, mn_out)
+
+
+def test_plain_full_size_sampled_rows():
+    m, n, k = 4096, 4096, 7168
+    say("plain full size", m, n, k)
+    d = workloads.plain(m, n, k, seed=0, device=DEV)
+    out = _plain_call(d)
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 255, 256, 2047, 2048, 4094, 4095],
+                                     rng.choice(m, 20, replace=False)]))
+    ref = _plain_ref(d, rows)
+    assert_within_tolerance(bf16_values(out)[rows], ref, "plain 4096x4096x7168 sampled rows")
+    assert not untouched(out).any()
+
+
+def _exact_case(m, n, k, seed):
+    """Codes in {0, +-1, +-2} and power-of-two scales: every partial sum is exact in FP32."""
+    rng = np.random.default_rng(seed)
+    pal = np.array([0x00, 0x38, 0xB8, 0x40, 0xC0], np.uint8)
+    a = pal[rng.integers(0, 5, (m, k))]
+    b = pal[rng.integers(0, 5, (n, k))]
+    sa = np.ldexp(1.0, rng.integers(-3, 4, (m, k // 128))).astype(np.float32)
+    sb = np.ldexp(1.0, rng.integers(-3, 4, (n // 128, k // 128))).astype(np.float32)
+    return a, b, sa, sb
+
+
+def test_plain_power_of_two_scales_are_bit_exact():
+    m, n, k = 257, 384, 1024
+    say("plain bit-exact", m, n, k)
+    a, b, sa, sb = _exact_case(m, n, k, 3)
+    t = lambda x: torch.from_numpy(x).to(DEV)
+    out = sentinel_like((m, n), DEV)
+    fp8g.fp8_gemm_nt_groupwise(t(a), t(b), t(sa), t(sb), out)
+    torch.cuda.synchronize()
+    want = bf16.to_bf16_bits(ogemm.gemm_fp8_nt_groupwise(a, b, sa, sb))
+    assert np.array_equal(host(out), want)
+
+
+def test_all_ones_closed_form():
+    m, n, k = 128, 256, 512
+    say("plain all ones", m, n, k)
+    alpha, beta = np.float32(0.375), np.float32(1.25)
+    a = torch.full((m, k), 0x38, dtype=torch.uint8, device=DEV)
+    b = torch.full((n, k), 0x38, dtype=torch.uint8, device=DEV)
+    sa = torch.full((m, k // 128), float(alpha), device=DEV)
+    sb = torch.full((n // 128, k // 128), float(beta), device=DEV)
+    out = fp8g.gemm_fp8_nt_groupwise(a, b, sa, sb)
+    torch.cuda.synchronize()
+    assert np.all(bf16_values(out) == k * float(alpha) * float(beta))
+
+
+def test_k_zero_writes_zeros():
+    say("plain k=0")
+    a = torch.empty((5, 0), dtype=torch.uint8, device=DEV)
+    b = torch.empty((128, 0), dtype=torch.uint8, device=DEV)
+    out = sentinel_like((5, 128), DEV)
+    fp8g.fp8_gemm_nt_groupwise(a, b, torch.empty((5, 0), device=DEV), torch.empty((1, 0), device=DEV), out)
+    torch.cuda.synchronize()
+    assert np.all(bf16_values(out) == 0.0)
+
+
+def test_p3_wrapper_scalar_b_scale_and_preallocated_out():
+    m, n, k = 64, 256, 256
+    say("plain wrapper scalar b_scale", m, n, k)
+    d = workloads.plain(m, n, k, seed=11, device=DEV)
+    out = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    got = fp8g.gemm_fp8_nt_groupwise(d["a"].view(torch.float8_e4m3fn), d["b"], d["a_scale"],
+                                     torch.tensor(0.5, device=DEV), out=out)
+    torch.cuda.synchronize()
+    assert got is out
+    ref = ogemm.gemm_fp8_nt_groupwise(host(d["a"]), host(d["b"]), host(d["a_scale"]), np.float32(0.5))
+    assert_within_tolerance(bf16_values(out), ref, "scalar b_scale")
+
+
+def test_side_stream_ordering():
+    m, n, k = 512, 512, 512
+    say("plain on a side stream", m, n, k)
+    d = workloads.plain(m, n, k, seed=12, device=DEV)
+    s = torch.cuda.Stream()
+    out = sentinel_like((m, n), DEV)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fp8g.fp8_gemm_nt_groupwise(d["a"], d["b"], d["a_scale"], d["b_scale"], out)
+    s.synchronize()
+    assert_within_tolerance(bf16_values(out), _plain_ref(d), "side stream")
+
+
+# ---------------------------------------------------------------------------------------------
+# masked batched form
+
+
+def _masked_call(d, masked_m=None, expected_m=None, major="K"):
+    sa, sb = d["a_scale"], d["b_scale"]
+    if major == "MN":
+        sa, sb = sa.transpose(1, 2).contiguous(), sb.transpose(1, 2).contiguous()
+    mm = d["masked_m"] if masked_m is None else masked_m
+    out = sentinel_like((d["num_groups"], d["max_m"], d["n"]), DEV)
+    fp8g.fp8_batch_gemm_masked(d["a"], d["b"], sa, sb, mm, d["expected_m"] if expected_m is None else expected_m,
+                               out, major)
+    torch.cuda.synchronize()
+    return out
+
+
+def _masked_ref(d, masked_m, groups=None, rows=None):
+    return ogemm.batch_gemm_masked(host(d["a"]), host(d["b"]), host(d["a_scale"]), host(d["b_scale"]),
+                                   masked_m, groups=groups, rows=rows)
+
+
+@pytest.mark.parametrize("expected_m", [1, 128, 256])
+def test_masked_matches_oracle_and_leaves_other_rows(expected_m):
+    G, max_m, n, k = 4, 200, 384, 512
+    mm = np.array([0, 200, 77, 129], np.int32)
+    say("masked", G, max_m, n, k, mm.tolist(), "expected_m", expected_m)
+    d = workloads.masked(G, max_m, n, k, expected_m, seed=5, device=DEV, masked_m=mm)
+    out = _masked_call(d)
+    ref = _masked_ref(d, mm)
+    assert_within_tolerance(bf16_values(out), ref, "masked")
+    keep = untouched(out)
+    for g in range(G):
+        assert keep[g, mm[g]:].all(), f"group {g}: rows at or beyond masked_m were written"
+        assert not keep[g, :mm[g]].any()
+
+
+def test_masked_expected_m_never_changes_results():
+    G, max_m, n, k = 3, 256, 256, 384
+    mm = np.array([256, 100, 3], np.int32)
+    say("masked expected_m invariance")
+    d = workloads.masked(G, max_m, n, k, 128, seed=6, device=DEV, masked_m=mm)
+    outs = [host(_masked_call(d, expected_m=e)) for e in (0, 1, 64, 65, 128, 256, 10000)]
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_masked_ignores_poisoned_rows_beyond_masked_m():
+    G, max_m, n, k = 2, 160, 256, 256
+    mm = np.array([33, 150], np.int32)
+    say("masked with NaN codes and scales beyond masked_m")
+    d = workloads.masked(G, max_m, n, k, 64, seed=8, device=DEV, masked_m=mm)
+    clean = _masked_call(d)
+    for g in range(G):
+        d["a"][g, mm[g]:] = 0x7F
+        d["a_scale"][g, mm[g]:] = float("nan")
+    poisoned = _masked_call(d)
+    assert np.array_equal(host(clean), host(poisoned))
+
+
+def test_masked_counts_outside_range_are_clamped():
+    G, max_m, n, k = 2, 64, 128, 256
+    say("masked clamp")
+    d = workloads.masked(G, max_m, n, k, 32, seed=9, device=DEV, masked_m=np.array([300, -4], np.int32))
+    out = _masked_call(d)
+    ref = _masked_ref(d, np.array([64, 0]))
+    assert_within_tolerance(bf16_values(out), ref, "masked clamp")
+    assert untouched(out)[1].all()
+
+
+def test_masked_mn_major_bitwise_equal():
+    say("masked K vs MN")
+    d = workloads.masked(3, 96, 256, 384, 64, seed=10, device=DEV, masked_m=np.array([96, 50, 7], np.int32))
+    assert np.array_equal(host(_masked_call(d, major="K")), host(_masked_call(d, major="MN")))
+
+
+def test_masked_full_size_sampled():
+    say("masked full size 16x256 n=4096 k=7168")
+    d = workloads.masked(16, 256, 4096, 7168, 128, seed=0, device=DEV)
+    mm = host(d["masked_m"])
+    out = _masked_call(d)
+    vals = bf16_values(out)
+    keep = untouched(out)
+    rng = np.random.default_rng(1)
+    groups = [g for g in range(16) if mm[g] > 0][:6]
+    for g in range(16):
+        assert keep[g, mm[g]:].all() and not keep[g, :mm[g]].any()
+    rows = sorted(set([0, 1, 15, 16, 127, 128, 255]) | set(rng.integers(0, 256, 6).tolist()))
+    ref = _masked_ref(d, mm, groups=groups, rows=rows)
+    assert_within_tolerance(vals, ref, "masked full size sampled")
+
+
+# ---------------------------------------------------------------------------------------------
+# contiguous grouped form
+
+
+def _contig_call(d, major="K"):
+    sa, sb = d["a_scale"], d["b_scale"]
+    if major == "MN":
+        sa, sb = sa.t().contiguous(), sb.transpose(1, 2).contiguous()
+    out = sentinel_like((d["m"], d["n"]), DEV)
+    fp8g.fp8_group_gemm_contiguous(d["a"], d["b"], sa, sb, d["m_indices"], out, major)
+    torch.cuda.synchronize()
+    return out
+
+
+def _contig_ref(d, rows=None, col_blocks=None):
+    b, sb = host(d["b"]), host(d["b_scale"])
+    if col_blocks is not None:
+        cols = np.concatenate([np.arange(c * 128, c * 128 + 128) for c in col_blocks])
+        b, sb = b[:, cols], sb[:, col_blocks]
+    return ogemm.group_gemm_contiguous(host(d["a"]), b, host(d["a_scale"]), sb, host(d["m_indices"]), rows=rows)
+
+
+def test_contiguous_matches_oracle_and_skips_padding():
+    counts = [130, 0, 5, 300]
+    say("contiguous", counts)
+    d = workloads.contiguous(4, n=256, k=384, seed=4, device=DEV, counts=counts)
+    out = _contig_call(d)
+    ref = _contig_ref(d)
+    assert_within_tolerance(bf16_values(out), ref, "contiguous")
+    mi = host(d["m_indices"])
+    keep = untouched(out)
+    assert keep[mi < 0].all() and not keep[mi >= 0].any()
+
+
+def test_contiguous_trailing_padding_tiles_and_poisoned_padding_rows():
+    counts = [3, 129]
+    say("contiguous trailing padding", counts)
+    d = workloads.contiguous(2, n=128, k=256, seed=5, device=DEV, counts=counts)
+    # two extra all-padding tiles at the end, and NaN codes/scales in every padding row
+    extra = 256
+    d["m_indices"] = torch.cat([d["m_indices"], torch.full((extra,), -1, dtype=torch.int32, device=DEV)])
+    d["a"] = torch.cat([d["a"], torch.full((extra, 256), 0x7F, dtype=torch.uint8, device=DEV)])
+    d["a_scale"] = torch.cat([d["a_scale"], torch.full((extra, 2), float("nan"), device=DEV)])
+    d["m"] += extra
+    pad = d["m_indices"] < 0
+    d["a"][pad] = 0x7F
+    d["a_scale"][pad] = float("nan")
+    out = _contig_call(d)
+    ref = _contig_ref(d)
+    assert_within_tolerance(bf16_values(out), ref, "contiguous with padding")
+    assert untouched(out)[host(pad)].all()
+
+
+def test_contiguous_mn_major_bitwise_equal():
+    say("contiguous K vs MN")
+    d = workloads.contiguous(3, n=256, k=512, seed=6, device=DEV, counts=[200, 64, 1])
+    assert np.array_equal(host(_contig_call(d, "K")), host(_contig_call(d, "MN")))
+
+
+def test_contiguous_full_size_sampled():
+    say("contiguous full size: 32 Zipf experts, 8192 rows, n=4096, k=7168")
+    d = workloads.contiguous(32, 8192, 4096, 7168, 1.1, seed=0, device=DEV)
+    out = _contig_call(d)
+    mi = host(d["m_indices"])
+    keep = untouched(out)
+    assert keep[mi < 0].all() and not keep[mi >= 0].any()
+    rng = np.random.default_rng(2)
+    rows = []
+    for e in (0, 1, 2, 7, 19, 31):
+        r = np.nonzero(mi == e)[0]
+        rows += [r[0], r[-1], r[len(r) // 2]]
+    rows += rng.choice(np.nonzero(mi >= 0)[0], 6, replace=False).tolist()
+    rows = np.unique(np.array(rows))
+    col_blocks = [0, 13, 31]
+    ref = _contig_ref(d, rows=rows, col_blocks=col_blocks)
+    cols = np.concatenate([np.arange(c * 128, c * 128 + 128) for c in col_blocks])
+    assert_within_tolerance(bf16_values(out)[rows][:, cols], ref, "contiguous full size sampled")

@@ -1,0 +1,140 @@
+"""GPU parity of the expert-FFN steps against the oracle, stage by stage (MI355X only).
+
+Integer work (the permutation) and the BF16 -> E4M3 quantiser of the tokens are compared bit for
+bit. The SiLU-mul quantiser is compared against the oracle fed the GPU's own fc1 output: both sides
+take the rounding decision in FP32, but SiLU's exp may differ by an ulp, so a code may differ by one
+step where the oracle's scaled value lies within a few FP32 ulps of the midpoint between two codes;
+every other code and every scale must match. The GEMMs and the combine are held to the GEMM
+tolerance on the oracle fed the GPU's own inputs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_matmul_amd as fp8g
+import workloads
+from oracle import bf16, e4m3, gemm as ogemm, moe as omoe
+from parity import assert_within_tolerance, bf16_values, host, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _run(d):
+    ws = fp8g.MoeWorkspace.allocate(d["num_tokens"], d["top_k"], d["num_experts"], d["hidden"], d["inter"], DEV)
+    out = fp8g.moe_ffn_fp8_block_scale(d["x"], d["topk_ids"], d["topk_weights"], d["w1"], d["s1"], d["w2"],
+                                       d["s2"], workspace=ws)
+    torch.cuda.synchronize()
+    return out, ws
+
+
+def _check_permutation(d, ws):
+    p = omoe.build_permutation(host(d["topk_ids"]), d["num_experts"], ws.m_alloc)
+    assert np.array_equal(host(ws.m_indices), p["m_indices"])
+    assert np.array_equal(host(ws.src_token), p["src_token"])
+    assert np.array_equal(host(ws.row_of_entry), p["row_of_entry"])
+    return p
+
+
+def _check_gather_quant(d, ws, p):
+    xq, xs = omoe.quantize_1x128(bf16.from_bf16_bits(host(d["x"])).astype(np.float32))
+    valid = p["src_token"] >= 0
+    src = p["src_token"][valid]
+    assert np.array_equal(host(ws.sa1)[valid], xs[src])
+    assert np.array_equal(host(ws.a1)[valid], xq[src])
+
+
+def _sliced_ref(a, sa, b, sb, m_indices, rows, col_blocks):
+    cols = np.concatenate([np.arange(c * 128, c * 128 + 128) for c in col_blocks])
+    return ogemm.group_gemm_contiguous(a, b[:, cols], sa, sb[:, col_blocks], m_indices, rows=rows), cols
+
+
+def _check_requant(y1_rows, a2_rows, sa2_rows):
+    """Oracle quantiser on the GPU's fc1 rows; allows one-step flips at FP32 rounding midpoints."""
+    h32 = omoe.silu_mul(bf16.from_bf16_bits(y1_rows)).astype(np.float32)
+    oc, osc = omoe.quantize_1x128(h32)
+    assert np.allclose(sa2_rows, osc, rtol=4e-7, atol=0), "requant scales differ by more than an ulp"
+    diff = a2_rows != oc
+    if diff.any():
+        x = (h32 / np.repeat(osc, 128, axis=1))[diff].astype(np.float64)
+        g = e4m3.decode(a2_rows[diff])
+        o = e4m3.decode(oc[diff])
+        mid = (g + o) / 2
+        assert np.all(np.abs(np.abs(g) - np.abs(o)) <= np.maximum(np.abs(g), np.abs(o)) / 8 + 2.0 ** -9)
+        assert np.all(np.abs(x - mid) <= 1e-5 * np.abs(x) + 1e-12), "a code differs away from a rounding midpoint"
+        assert diff.mean() <= 1e-3
+    return int(diff.sum())
+
+
+def _stagewise(d, out, ws, p, rows, token_sample, col_blocks_fc1, col_blocks_fc2):
+    mi = p["m_indices"]
+    w1, s1, w2, s2 = host(d["w1"]), host(d["s1"]), host(d["w2"]), host(d["s2"])
+    a1, sa1 = host(ws.a1), host(ws.sa1)
+    y1_bits = host(ws.y1)
+    # fc1 on the GPU's own permuted activations
+    ref, cols = _sliced_ref(a1, sa1, w1, s1, mi, rows, col_blocks_fc1)
+    assert_within_tolerance(bf16.from_bf16_bits(y1_bits[rows][:, cols]), ref, "fc1")
+    # SiLU-mul + requant on the GPU's own fc1 output
+    flips = _check_requant(y1_bits[rows], host(ws.a2)[rows], host(ws.sa2)[rows])
+    # fc2 on the GPU's own requantised activations
+    ref, cols = _sliced_ref(host(ws.a2), host(ws.sa2), w2, s2, mi, rows, col_blocks_fc2)
+    assert_within_tolerance(bf16.from_bf16_bits(host(ws.y2)[rows][:, cols]), ref, "fc2")
+    # combine on the GPU's own fc2 output (only the rows the sampled tokens read are converted)
+    roe = p["row_of_entry"][token_sample]
+    y2_rows = bf16.from_bf16_bits(host(ws.y2)[np.maximum(roe.reshape(-1), 0)])
+    compact = np.where(roe >= 0, np.arange(roe.size).reshape(roe.shape), -1)
+    ref = omoe.combine(y2_rows, compact, host(d["topk_weights"])[token_sample])
+    assert_within_tolerance(bf16_values(out)[token_sample], ref, "combine")
+    return flips
+
+
+def test_moe_small_all_stages_and_end_to_end():
+    say("moe small T=256 H=512 E=8 k=2 I=256")
+    d = workloads.moe(num_tokens=256, hidden=512, num_experts=8, top_k=2, inter=256, seed=1, device=DEV)
+    out, ws = _run(d)
+    p = _check_permutation(d, ws)
+    _check_gather_quant(d, ws, p)
+    rows = np.nonzero(p["m_indices"] >= 0)[0]
+    flips = _stagewise(d, out, ws, p, rows, np.arange(256), [0, 1, 2, 3], [0, 1, 2, 3])
+    say("requant code flips", flips)
+    # end to end against the all-oracle chain: reported, and every output within the tolerance
+    r = omoe.moe_ffn(bf16.from_bf16_bits(host(d["x"])), host(d["topk_ids"]), host(d["topk_weights"]),
+                     host(d["w1"]), host(d["s1"]), host(d["w2"]), host(d["s2"]), m_alloc=ws.m_alloc)
+    assert_within_tolerance(bf16_values(out), r["out"], "moe end to end")
+
+
+def test_moe_unrouted_entries_and_empty_experts():
+    say("moe with dropped entries and experts without tokens")
+    d = workloads.moe(num_tokens=64, hidden=256, num_experts=6, top_k=2, inter=128, seed=2, device=DEV)
+    ids = host(d["topk_ids"]).copy()
+    ids[ids == 3] = 4          # expert 3 gets no rows
+    ids[5, 1] = -1             # entries routed nowhere
+    ids[9, 0] = 6
+    d["topk_ids"] = torch.from_numpy(ids).to(DEV)
+    out, ws = _run(d)
+    p = _check_permutation(d, ws)
+    assert p["counts"][3] == 0
+    assert host(ws.row_of_entry)[5, 1] == -1 and host(ws.row_of_entry)[9, 0] == -1
+    _check_gather_quant(d, ws, p)
+    rows = np.nonzero(p["m_indices"] >= 0)[0]
+    _stagewise(d, out, ws, p, rows, np.arange(64), [0, 1], [0, 1])
+
+
+def test_moe_full_size_stagewise_sampled():
+    say("moe full size T=4096 H=7168 E=64 k=8 I=2048")
+    d = workloads.moe(seed=0, device=DEV)
+    out, ws = _run(d)
+    p = _check_permutation(d, ws)
+    _check_gather_quant(d, ws, p)
+    mi = p["m_indices"]
+    rng = np.random.default_rng(3)
+    rows = []
+    for e in (0, 17, 63):
+        r = np.nonzero(mi == e)[0]
+        rows += [r[0], r[-1]]
+    rows += rng.choice(np.nonzero(mi >= 0)[0], 6, replace=False).tolist()
+    rows = np.unique(np.array(rows))
+    tokens = np.unique(np.concatenate([[0, 4095], rng.choice(4096, 14, replace=False)]))
+    flips = _stagewise(d, out, ws, p, rows, tokens, [0, 16, 31], [0, 27, 55])
+    say("requant code flips on sampled rows", flips)
