@@ -170,6 +170,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--configs", action="store_true", help="also time the grouped, masked and expert-FFN workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run five 1 GiB device-to-device copies (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU sharding is not built",
@@ -182,6 +184,14 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "5 copies of 1 GiB (1073741824 B read + 1073741824 B written each)"}))
+        return
     m = n = 4096
     k = 7168
     d = workloads.plain(m, n, k, seed=0, device=dev)

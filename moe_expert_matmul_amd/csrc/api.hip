@@ -10,6 +10,7 @@
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <exception>
 #include <string>
@@ -114,8 +115,9 @@ void check_gemm_dims(int64_t rows, int64_t n, int64_t k) {
 }
 
 void check_operands(const void* a, const void* b, const float* sa, const float* sb, const void* out, int64_t k) {
-  require(a && b && out, "a, b and out must be non-null");
-  require(k == 0 || (sa && sb), "a_scale and b_scale must be non-null");
+  // with k == 0 the operands and scales are empty and may be null; out is still written
+  require(out != nullptr, "out must be non-null");
+  require(k == 0 || (a && b && sa && sb), "a, b, a_scale and b_scale must be non-null");
   require(aligned(a, 16) && aligned(b, 16) && aligned(out, 16), "a, b and out must be 16-byte aligned");
   require(aligned(sa, 4) && aligned(sb, 4), "scales must be 4-byte aligned");
 }
@@ -138,6 +140,18 @@ void set_scale_strides(fp8g::GemmParams& p, int32_t scale_major, int64_t rows) {
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
+
+int fp8g::tile_override() {
+  static const int value = [] {
+    const char* e = std::getenv("FP8G_TILE");
+    if (!e) return -1;
+    if (!std::strcmp(e, "256x256")) return (int)TILE_256x256;
+    if (!std::strcmp(e, "128x256")) return (int)TILE_128x256;
+    if (!std::strcmp(e, "256x128")) return (int)TILE_256x128;
+    return -1;
+  }();
+  return value;
+}
 
 extern "C" {
 
@@ -169,7 +183,8 @@ fp8g_status_t fp8_gemm_nt_groupwise(const void* a, const void* b, const float* a
     p.nblocks = (int32_t)(n / 128);
     p.num_groups = 1;
     set_scale_strides(p, scale_major, m);
-    const fp8g::TileConfig cfg = m > 128 ? fp8g::TILE_256x256 : fp8g::TILE_128x256;
+    fp8g::TileConfig cfg = m > 128 ? fp8g::TILE_256x256 : fp8g::TILE_128x256;
+    if (fp8g::tile_override() >= 0) cfg = (fp8g::TileConfig)fp8g::tile_override();
     p.tiles_m = (int32_t)ceil_div(m, fp8g::tile_rows(cfg));
     p.tiles_n = (int32_t)ceil_div(n, fp8g::tile_cols(cfg));
     p.group_m = 4;
@@ -257,8 +272,8 @@ fp8g_status_t fp8_batch_gemm_masked(const void* a, const void* b, const float* a
     set_scale_strides(p, scale_major, max_m);
     // expected_m picks the row tile: one 256-row tile per group reads each b tile once; smaller
     // expected groups use 128-row tiles so that the second row tile is usually skipped.
-    const fp8g::TileConfig cfg =
-        (max_m > 128 && expected_m > 64) ? fp8g::TILE_256x256 : fp8g::TILE_128x256;
+    fp8g::TileConfig cfg = (max_m > 128 && expected_m > 64) ? fp8g::TILE_256x256 : fp8g::TILE_128x256;
+    if (fp8g::tile_override() >= 0) cfg = (fp8g::TileConfig)fp8g::tile_override();
     p.tiles_m = (int32_t)ceil_div(max_m, fp8g::tile_rows(cfg));
     p.tiles_n = (int32_t)ceil_div(n, fp8g::tile_cols(cfg));
     p.group_m = p.tiles_m;

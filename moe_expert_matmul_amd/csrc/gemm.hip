@@ -17,9 +17,10 @@
 // Data movement per workgroup and K block: the BMx128 slab of a and the BNx128 slab of b go from
 // HBM straight into LDS (global_load_lds_dwordx4, no VGPR staging), double-buffered so the loads of
 // block kb+1 overlap the MFMAs of block kb. Rows are 128 bytes in LDS with their 16-byte chunks
-// XOR-swizzled by (row & 7), so the 16 lanes reading one chunk column of 16 rows hit distinct banks.
-// The swizzle is applied on the global side: lane l of a load writes LDS chunk l of its 1 KB slab
-// and fetches the logical chunk that belongs there.
+// XOR-swizzled by ((row >> 1) & 7), which spreads the 16 rows of a fragment over all 64 four-byte
+// banks; together with the fragment's chunk assignment (see load_frag) a fragment read runs at the
+// LDS's full rate. The swizzle is applied on the global side: lane l of a load writes LDS chunk l of
+// its 1 KB slab and fetches the logical chunk that belongs there.
 //
 // Tile scheduling: the 1-D grid is renumbered so that consecutive tiles run on the same XCD (the
 // hardware deals workgroups round-robin over the 8 XCDs, each with its own L2) and then rasterised
@@ -42,7 +43,12 @@ constexpr int SLAB_ROWS = 8;      // rows filled by one wave-wide 16-byte-per-la
 constexpr int E8M0_ONE = 127;     // 2^0 as an E8M0 block scale
 constexpr int FMT_E4M3 = 0;       // f8f6f4 operand format code of FP8 E4M3
 
-template <int BM, int BN, int WM, int WN>
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int SG_VALU = 0x002;
+constexpr int SG_MFMA = 0x008;
+constexpr int SG_DS_READ = 0x100;
+
+template <int BM, int BN, int WM, int WN, int STAGES>
 struct Tile {
   static constexpr int NWAVES = WM * WN;
   static constexpr int NTHREADS = NWAVES * 64;
@@ -52,20 +58,50 @@ struct Tile {
   static constexpr int JG = WTN / 16;
   static constexpr int A_BYTES = BM * KBLK;
   static constexpr int B_BYTES = BN * KBLK;
-  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int SA_OFF = A_BYTES + B_BYTES;  // BM floats: a's scales of the K block
+  static constexpr int SB_OFF = SA_OFF + BM * 4;    // 64 floats: b's scales (BN/128 used)
+  static constexpr int STAGE_BYTES = SB_OFF + 64 * 4;
   static constexpr int A_LOADS = BM / SLAB_ROWS / NWAVES;  // per wave and K block
   static constexpr int B_LOADS = BN / SLAB_ROWS / NWAVES;
+  static constexpr int LOADS = A_LOADS + B_LOADS + 1;      // + one scale load per wave
+  static_assert(BM / 64 < NWAVES, "one wave per 64 a-scale rows, and one more for b's scales");
+  static_assert(STAGE_BYTES % 256 == 0, "stages keep the slabs' bank alignment");
   static_assert(BM % (SLAB_ROWS * NWAVES) == 0 && BN % (SLAB_ROWS * NWAVES) == 0, "slabs");
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "16x16 MFMA blocks");
   static_assert(128 % WTN == 0, "a wave's columns must sit in one 128-wide b-scale block");
+  static_assert(STAGES == 2 || STAGES == 3, "two or three LDS stages");
+  static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
 };
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4, lgkmcnt 11:8). A real S_WAITCNT, so the compiler's own wait insertion sees it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for the LDS pipeline. The LDS reads of this wave are retired first
+// (lgkmcnt(0)) so a stage can be refilled after it; the slab loads' visibility is handled by the
+// caller's vmcnt wait. Unlike __syncthreads() it carries no release fence, which would drain every
+// load in flight, including the ones meant to stay in flight across the barrier. The empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_pipeline_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maximum
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4). The LDS
 // address is wave-uniform: lane l writes bytes [16l, 16l+16) of the 1 KB block at `lds`.
 __device__ __forceinline__ void load_lds_16(const uint8_t* gsrc, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds(const_cast<uint8_t*>(gsrc), lds, 16, 0, 0);
+}
+
+// 4 bytes per lane into LDS (global_load_lds_dword): lane l writes bytes [4l, 4l+4) at `lds`.
+__device__ __forceinline__ void load_lds_4(const float* gsrc, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(const_cast<float*>(gsrc), lds, 4, 0, 0);
 }
 
 __device__ __forceinline__ int wave_max(int v) {
@@ -90,26 +126,30 @@ __device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int grou
   tn = r / gm;
 }
 
-// One 16x128 FP8 operand fragment: lane l supplies row (l & 15) of the 16-row group and the 32
-// bytes at K offset 32*(l >> 4) of the K block. Both operands use the same K assignment, which is
-// all the matrix core needs for a dot product over the block.
+// Physical 16-byte chunk of logical chunk c in tile row r is c ^ swizzle(r).
+__device__ __forceinline__ int swizzle(int row) { return (row >> 1) & 7; }
+
+// One 16x128 FP8 operand fragment: lane l supplies row (l & 15) of the 16-row group and the 16-byte
+// chunks g and g+4 of the K block, g = l >> 4. Both operands use the same K assignment, which is
+// all the matrix core needs for a dot product over the block. (Lane groups reading chunks g and
+// g+4 keep each ds_read_b128 free of bank conflicts; chunks 2g and 2g+1 measured half the rate.)
 __device__ __forceinline__ i32x8 load_frag(const uint8_t* slab, int row, int lane) {
   const uint8_t* rp = slab + row * KBLK;
-  const int c0 = (lane >> 4) * 2;
-  const int sw = row & 7;
+  const int c0 = lane >> 4;
+  const int sw = swizzle(row);
   const i32x4 lo = *reinterpret_cast<const i32x4*>(rp + ((c0 ^ sw) << 4));
-  const i32x4 hi = *reinterpret_cast<const i32x4*>(rp + (((c0 + 1) ^ sw) << 4));
+  const i32x4 hi = *reinterpret_cast<const i32x4*>(rp + (((c0 + 4) ^ sw) << 4));
   return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
-template <int BM, int BN, int WM, int WN, int MODE>
+template <int BM, int BN, int WM, int WN, int STAGES, int MODE>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_fp8_groupwise_kernel(const GemmParams p) {
-  using T = Tile<BM, BN, WM, WN>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::STAGE_BYTES];
+  using T = Tile<BM, BN, WM, WN, STAGES>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * T::STAGE_BYTES];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in an SGPR
 
   // ---- tile scheduling ---------------------------------------------------------------------
   int t = xcd_local_order(blockIdx.x, gridDim.x);
@@ -145,40 +185,48 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   const float* SB = p.sb + (int64_t)bsel * p.sb_group_stride;
 
   // ---- HBM -> LDS load assignment ----------------------------------------------------------
-  // Slab s (1 KB) holds tile rows [8s, 8s+8); lane l fills its chunk l, i.e. row 8s + (l>>3),
-  // physical chunk (l & 7), which holds logical chunk (l & 7) ^ (l >> 3).
+  // Slab s (1 KB) holds tile rows [8s, 8s+8); lane l fills its chunk l, i.e. tile row
+  // 8s + (l >> 3) at physical chunk (l & 7), which holds logical chunk (l & 7) ^ swizzle(row).
+  // Every wave issues the same number of loads for every K block (rows past the valid range are
+  // clamped to the last valid row), so the pipeline can wait on a fixed count of outstanding loads.
   const int lrow = lane >> 3;
-  const int lchunk = (lane & 7) ^ lrow;
+  const int a_last = row_end - 1;
   uint32_t a_off[T::A_LOADS], b_off[T::B_LOADS];
-  bool a_live[T::A_LOADS], b_live[T::B_LOADS];
 #pragma unroll
   for (int q = 0; q < T::A_LOADS; ++q) {
     const int slab_row = (wave * T::A_LOADS + q) * SLAB_ROWS;
-    const int r = min(row0 + slab_row + lrow, p.m - 1);
+    const int lchunk = (lane & 7) ^ swizzle(slab_row + lrow);
+    const int r = min(row0 + slab_row + lrow, a_last);
     a_off[q] = (uint32_t)r * (uint32_t)p.k + lchunk * 16;
-    a_live[q] = row0 + slab_row < row_end;
   }
 #pragma unroll
   for (int q = 0; q < T::B_LOADS; ++q) {
     const int slab_row = (wave * T::B_LOADS + q) * SLAB_ROWS;
+    const int lchunk = (lane & 7) ^ swizzle(slab_row + lrow);
     const int r = min(col0 + slab_row + lrow, p.n - 1);
     b_off[q] = (uint32_t)r * (uint32_t)p.k + lchunk * 16;
-    b_live[q] = col0 + slab_row < p.n;
   }
 
-  // ---- this wave's output block and scale addressing -----------------------------------------
+  // Scales of a K block travel with its slabs: waves 0 .. BM/64-1 each fetch 64 of a's row
+  // scales, every other wave fetches b's BN/128 block scales (identical data to the same place).
+  const float* s_src;
+  int s_dst;
+  if (wave < BM / 64) {
+    const int r = min(row0 + wave * 64 + lane, p.m - 1);
+    s_src = SA + r * p.sa_row_stride;
+    s_dst = T::SA_OFF + wave * 256;
+  } else {
+    const int nb = min(col0 / 128 + lane, p.nblocks - 1);
+    s_src = SB + nb * p.sb_nb_stride;
+    s_dst = T::SB_OFF;
+  }
+  const int s_kb_stride = wave < BM / 64 ? p.sa_kb_stride : p.sb_kb_stride;
+
+  // ---- this wave's output block --------------------------------------------------------------
   const int i0 = (wave % WM) * T::WTM;
   const int j0 = (wave / WM) * T::WTN;
   const bool wave_live = (row0 + i0 < row_end) && (col0 + j0 < p.n);
   const int fr = lane & 15;
-  int sa_off[T::IG];
-#pragma unroll
-  for (int ig = 0; ig < T::IG; ++ig) {
-    const int r = min(row0 + i0 + ig * 16 + fr, p.m - 1);
-    sa_off[ig] = r * p.sa_row_stride;
-  }
-  const int nb = min((col0 + j0) / 128, p.nblocks - 1);
-  const int sb_off = nb * p.sb_nb_stride;
 
   f32x4 acc[T::IG][T::JG];
 #pragma unroll
@@ -186,65 +234,87 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
 #pragma unroll
     for (int jg = 0; jg < T::JG; ++jg) acc[ig][jg] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto issue_loads = [&](int kb, int stage) {
-    uint8_t* sA = smem + stage * T::STAGE_BYTES;
+  auto issue_loads = [&](int kb) {
+    uint8_t* sA = smem + (kb % STAGES) * T::STAGE_BYTES;
     uint8_t* sB = sA + T::A_BYTES;
     const uint32_t koff = (uint32_t)kb * KBLK;
 #pragma unroll
-    for (int q = 0; q < T::A_LOADS; ++q)
-      if (a_live[q])
-        load_lds_16(A + a_off[q] + koff, sA + (wave * T::A_LOADS + q) * 1024);
+    for (int q = 0; q < T::A_LOADS; ++q) load_lds_16(A + a_off[q] + koff, sA + (wave * T::A_LOADS + q) * 1024);
 #pragma unroll
-    for (int q = 0; q < T::B_LOADS; ++q)
-      if (b_live[q])
-        load_lds_16(B + b_off[q] + koff, sB + (wave * T::B_LOADS + q) * 1024);
+    for (int q = 0; q < T::B_LOADS; ++q) load_lds_16(B + b_off[q] + koff, sB + (wave * T::B_LOADS + q) * 1024);
+    load_lds_4(s_src + kb * s_kb_stride, sA + s_dst);
   };
 
-  float sa_next[T::IG];
-  float sb_next = 0.f;
-  auto load_scales = [&](int kb) {
-#pragma unroll
-    for (int ig = 0; ig < T::IG; ++ig) sa_next[ig] = SA[sa_off[ig] + kb * p.sa_kb_stride];
-    sb_next = SB[sb_off + kb * p.sb_kb_stride];
-  };
-
+  // Pipeline: K block kb (slabs and scales) lives in stage kb % STAGES. Iteration kb waits until
+  // its own loads, issued STAGES-1 iterations earlier, have landed -- with three stages the loads of
+  // kb+1 stay in flight -- synchronises the workgroup (which also retires every read of the stage
+  // about to be refilled), issues the loads of kb+STAGES-1 and computes. No load in the loop
+  // targets a register, so nothing else makes the wave wait on memory.
   const int KB = p.kblocks;
-  if (KB > 0) {
-    issue_loads(0, 0);
-    load_scales(0);
-  }
-  wait_vmem();
-  __syncthreads();
+  if (KB > 0) issue_loads(0);
+  if (STAGES == 3 && KB > 1) issue_loads(1);
 
   for (int kb = 0; kb < KB; ++kb) {
-    const int stage = kb & 1;
-    float s[T::IG];
-#pragma unroll
-    for (int ig = 0; ig < T::IG; ++ig) s[ig] = sa_next[ig] * sb_next;
-    if (kb + 1 < KB) {
-      issue_loads(kb + 1, stage ^ 1);
-      load_scales(kb + 1);
-    }
+    if (STAGES == 3 && kb + 1 < KB)
+      wait_vmcnt<T::LOADS>();  // the newest group in flight is the loads of kb+1
+    else
+      wait_vmcnt<0>();
+    lds_pipeline_barrier();
+    if (kb + STAGES - 1 < KB) issue_loads(kb + STAGES - 1);
     if (wave_live) {
-      const uint8_t* sA = smem + stage * T::STAGE_BYTES;
+      const uint8_t* sA = smem + (kb % STAGES) * T::STAGE_BYTES;
       const uint8_t* sB = sA + T::A_BYTES;
+      const float* sSA = reinterpret_cast<const float*>(sA + T::SA_OFF);
+      const float sbv = reinterpret_cast<const float*>(sA + T::SB_OFF)[(col0 + j0) / 128 - col0 / 128];
+      float s[T::IG];
+#pragma unroll
+      for (int ig = 0; ig < T::IG; ++ig) s[ig] = sSA[i0 + ig * 16 + fr] * sbv;
+      // Software pipeline over the wave's column groups: the MFMAs of group jg are issued while
+      // the FMAs that promote group jg-1 retire, and the b fragment of group jg+1 is read from LDS
+      // meanwhile, so the matrix core never waits on a VALU read of its own result.
       i32x8 af[T::IG];
 #pragma unroll
       for (int ig = 0; ig < T::IG; ++ig) af[ig] = load_frag(sA, i0 + ig * 16 + fr, lane);
+      i32x8 bcur = load_frag(sB, j0 + fr, lane);
+      f32x4 pend[T::IG];
 #pragma unroll
       for (int jg = 0; jg < T::JG; ++jg) {
-        const i32x8 bfr = load_frag(sB, j0 + jg * 16 + fr, lane);
+        i32x8 bnext;
+        if (jg + 1 < T::JG) bnext = load_frag(sB, j0 + (jg + 1) * 16 + fr, lane);
+        f32x4 prod[T::IG];
+#pragma unroll
+        for (int ig = 0; ig < T::IG; ++ig)
+          prod[ig] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              bcur, af[ig], f32x4{0.f, 0.f, 0.f, 0.f}, FMT_E4M3, FMT_E4M3, 0, E8M0_ONE, 0, E8M0_ONE);
+        if (jg > 0) {
+#pragma unroll
+          for (int ig = 0; ig < T::IG; ++ig)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[ig][jg - 1][r] = __builtin_fmaf(pend[ig][r], s[ig], acc[ig][jg - 1][r]);
+        }
+#pragma unroll
+        for (int ig = 0; ig < T::IG; ++ig) pend[ig] = prod[ig];
+        if (jg + 1 < T::JG) bcur = bnext;
+      }
+#pragma unroll
+      for (int ig = 0; ig < T::IG; ++ig)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[ig][T::JG - 1][r] = __builtin_fmaf(pend[ig][r], s[ig], acc[ig][T::JG - 1][r]);
+      // Issue order for the block above: the a fragments and the first b fragment, then per
+      // column group its next b fragment followed by (one MFMA, four VALU) x IG, then the last
+      // group's promotion.
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * T::IG + 2 + T::IG + 1, 0);
+#pragma unroll
+      for (int jg = 0; jg < T::JG; ++jg) {
+        if (jg + 1 < T::JG) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
 #pragma unroll
         for (int ig = 0; ig < T::IG; ++ig) {
-          const f32x4 pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              bfr, af[ig], f32x4{0.f, 0.f, 0.f, 0.f}, FMT_E4M3, FMT_E4M3, 0, E8M0_ONE, 0, E8M0_ONE);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[ig][jg][r] = __builtin_fmaf(pr[r], s[ig], acc[ig][jg][r]);
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_VALU, 4, 0);
         }
       }
+      __builtin_amdgcn_sched_group_barrier(SG_VALU, 4 * T::IG, 0);
     }
-    wait_vmem();
-    __syncthreads();
   }
 
   // ---- epilogue: BF16 round-to-nearest-even, 8-byte stores of valid rows ---------------------
@@ -272,18 +342,18 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int STAGES>
 hipError_t launch_cfg(GemmMode mode, const GemmParams& p, int grid, hipStream_t stream) {
   const dim3 block(WM * WN * 64);
   switch (mode) {
     case MODE_PLAIN:
-      hipLaunchKernelGGL((gemm_fp8_groupwise_kernel<BM, BN, WM, WN, MODE_PLAIN>), dim3(grid), block, 0, stream, p);
+      hipLaunchKernelGGL((gemm_fp8_groupwise_kernel<BM, BN, WM, WN, STAGES, MODE_PLAIN>), dim3(grid), block, 0, stream, p);
       break;
     case MODE_CONTIG:
-      hipLaunchKernelGGL((gemm_fp8_groupwise_kernel<BM, BN, WM, WN, MODE_CONTIG>), dim3(grid), block, 0, stream, p);
+      hipLaunchKernelGGL((gemm_fp8_groupwise_kernel<BM, BN, WM, WN, STAGES, MODE_CONTIG>), dim3(grid), block, 0, stream, p);
       break;
     case MODE_MASKED:
-      hipLaunchKernelGGL((gemm_fp8_groupwise_kernel<BM, BN, WM, WN, MODE_MASKED>), dim3(grid), block, 0, stream, p);
+      hipLaunchKernelGGL((gemm_fp8_groupwise_kernel<BM, BN, WM, WN, STAGES, MODE_MASKED>), dim3(grid), block, 0, stream, p);
       break;
   }
   return hipGetLastError();
@@ -293,12 +363,16 @@ hipError_t launch_cfg(GemmMode mode, const GemmParams& p, int grid, hipStream_t 
 
 using namespace kernels;
 
-int tile_rows(TileConfig cfg) { return cfg == TILE_256x256 ? 256 : 128; }
-int tile_cols(TileConfig cfg) { return 256; }
+int tile_rows(TileConfig cfg) { return cfg == TILE_128x256 ? 128 : 256; }
+int tile_cols(TileConfig cfg) { return cfg == TILE_256x128 ? 128 : 256; }
 
 hipError_t launch_gemm(GemmMode mode, TileConfig cfg, GemmParams p, int grid, hipStream_t stream) {
-  if (cfg == TILE_256x256) return launch_cfg<256, 256, 4, 2>(mode, p, grid, stream);
-  return launch_cfg<128, 256, 2, 4>(mode, p, grid, stream);
+  switch (cfg) {
+    case TILE_256x256: return launch_cfg<256, 256, 4, 2, 2>(mode, p, grid, stream);
+    case TILE_128x256: return launch_cfg<128, 256, 2, 4, 3>(mode, p, grid, stream);
+    case TILE_256x128: return launch_cfg<256, 128, 4, 2, 3>(mode, p, grid, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fp8g

@@ -33,9 +33,14 @@ struct GemmParams {
 
 // Tile configurations the host may pick. Results are identical for every configuration.
 enum TileConfig : int {
-  TILE_256x256 = 0,  // 8 waves as 4 (rows) x 2 (cols), 64x128 per wave
-  TILE_128x256 = 1,  // 8 waves as 2 x 4, 64x64 per wave
+  TILE_256x256 = 0,  // 8 waves as 4 (rows) x 2 (cols), 64x128 per wave, 2 LDS stages
+  TILE_128x256 = 1,  // 8 waves as 2 x 4, 64x64 per wave, 3 LDS stages
+  TILE_256x128 = 2,  // 8 waves as 4 x 2, 64x64 per wave, 3 LDS stages
 };
+
+// Tile configuration forced through the FP8G_TILE environment variable ("256x256", "128x256",
+// "256x128"), read once; -1 when unset. For tuning only: results never depend on the tile.
+int tile_override();
 
 int tile_rows(TileConfig cfg);
 int tile_cols(TileConfig cfg);

@@ -81,6 +81,8 @@ def test_unsupported_granularity_is_not_supported(lib):
 def test_null_and_misaligned_pointers_are_rejected(lib):
     st, msg = _status(lib.fp8_gemm_nt_groupwise, None, P, P, P, P, 4, 128, 128, 0, *GRAN, None)
     assert st == _lib.INVALID_ARGUMENT and "non-null" in msg
+    st, msg = _status(lib.fp8_gemm_nt_groupwise, P, P, P, P, None, 4, 128, 0, 0, *GRAN, None)
+    assert st == _lib.INVALID_ARGUMENT and "out must be non-null" in msg
     st, msg = _status(lib.fp8_gemm_nt_groupwise, ctypes.c_void_p(17), P, P, P, P, 4, 128, 128, 0, *GRAN, None)
     assert st == _lib.INVALID_ARGUMENT and "aligned" in msg
 
