@@ -47,6 +47,7 @@ constexpr int FMT_E4M3 = 0;       // f8f6f4 operand format code of FP8 E4M3
 constexpr int SG_VALU = 0x002;
 constexpr int SG_MFMA = 0x008;
 constexpr int SG_DS_READ = 0x100;
+constexpr int SG_VMEM = 0x010;
 
 template <int BM, int BN, int WM, int WN, int STAGES>
 struct Tile {
@@ -73,6 +74,25 @@ struct Tile {
   static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
 };
 
+// A sched_group_barrier of n (0..12) memory instructions; n folds to a constant after unrolling.
+__device__ __forceinline__ void sched_vmem_group(int n) {
+  switch (n) {
+    case 1: __builtin_amdgcn_sched_group_barrier(SG_VMEM, 1, 0); break;
+    case 2: __builtin_amdgcn_sched_group_barrier(SG_VMEM, 2, 0); break;
+    case 3: __builtin_amdgcn_sched_group_barrier(SG_VMEM, 3, 0); break;
+    case 4: __builtin_amdgcn_sched_group_barrier(SG_VMEM, 4, 0); break;
+    case 5: __builtin_amdgcn_sched_group_barrier(SG_VMEM, 5, 0); break;
+    case 6: __builtin_amdgcn_sched_group_barrier(SG_VMEM, 6, 0); break;
+    case 7: __builtin_amdgcn_sched_group_barrier(SG_VMEM, 7, 0); break;
+    case 8: __builtin_amdgcn_sched_group_barrier(SG_VMEM, 8, 0); break;
+    case 9: __builtin_amdgcn_sched_group_barrier(SG_VMEM, 9, 0); break;
+    case 10: __builtin_amdgcn_sched_group_barrier(SG_VMEM, 10, 0); break;
+    case 11: __builtin_amdgcn_sched_group_barrier(SG_VMEM, 11, 0); break;
+    case 12: __builtin_amdgcn_sched_group_barrier(SG_VMEM, 12, 0); break;
+    default: break;
+  }
+}
+
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt in bits 3:0 and
 // 15:14, expcnt 6:4, lgkmcnt 11:8). A real S_WAITCNT, so the compiler's own wait insertion sees it.
 template <int N>
@@ -93,15 +113,22 @@ __device__ __forceinline__ void lds_pipeline_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4). The LDS
-// address is wave-uniform: lane l writes bytes [16l, 16l+16) of the 1 KB block at `lds`.
-__device__ __forceinline__ void load_lds_16(const uint8_t* gsrc, uint8_t* lds) {
-  __builtin_amdgcn_global_load_lds(const_cast<uint8_t*>(gsrc), lds, 16, 0, 0);
+// Buffer resource (base, byte size) for the loads below; word 3 is the gfx9 raw-buffer format.
+// Accesses past `bytes` read zero instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// 4 bytes per lane into LDS (global_load_lds_dword): lane l writes bytes [4l, 4l+4) at `lds`.
-__device__ __forceinline__ void load_lds_4(const float* gsrc, uint8_t* lds) {
-  __builtin_amdgcn_global_load_lds(const_cast<float*>(gsrc), lds, 4, 0, 0);
+// 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 ... lds): lane l reads
+// byte offset voff + soff and writes bytes [16l, 16l+16) of the 1 KB block at the wave-uniform
+// address `lds`. soff is a scalar, so the per-lane offset is the only vector register used.
+__device__ __forceinline__ void load_lds_16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, 0);
+}
+
+// 4 bytes per lane into LDS: lane l writes bytes [4l, 4l+4) at `lds`.
+__device__ __forceinline__ void load_lds_4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, voff, soff, 0, 0);
 }
 
 __device__ __forceinline__ int wave_max(int v) {
@@ -146,6 +173,8 @@ template <int BM, int BN, int WM, int WN, int STAGES, int MODE>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_fp8_groupwise_kernel(const GemmParams p) {
   using T = Tile<BM, BN, WM, WN, STAGES>;
+  // first of the loads issued during column group jg (the LOADS loads spread over JG groups)
+  constexpr auto load_first = [](int jg) { return (jg * T::LOADS + T::JG - 1) / T::JG; };
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * T::STAGE_BYTES];
 
   const int lane = threadIdx.x & 63;
@@ -207,20 +236,29 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     b_off[q] = (uint32_t)r * (uint32_t)p.k + lchunk * 16;
   }
 
+  // Buffer resources of this tile's operands (per group for the grouped forms).
+  const uint32_t a_bytes = (uint32_t)p.m * (uint32_t)p.k;
+  const uint32_t b_bytes = (uint32_t)p.n * (uint32_t)p.k;
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(A, a_bytes);
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(B, b_bytes);
+
   // Scales of a K block travel with its slabs: waves 0 .. BM/64-1 each fetch 64 of a's row
   // scales, every other wave fetches b's BN/128 block scales (identical data to the same place).
-  const float* s_src;
+  const bool a_scale_wave = wave < BM / 64;
+  const __amdgpu_buffer_rsrc_t rS =
+      a_scale_wave ? make_rsrc(SA, (uint32_t)p.m * p.kblocks * 4) : make_rsrc(SB, (uint32_t)p.nblocks * p.kblocks * 4);
+  uint32_t s_voff;
   int s_dst;
-  if (wave < BM / 64) {
+  if (a_scale_wave) {
     const int r = min(row0 + wave * 64 + lane, p.m - 1);
-    s_src = SA + r * p.sa_row_stride;
+    s_voff = (uint32_t)r * p.sa_row_stride * 4;
     s_dst = T::SA_OFF + wave * 256;
   } else {
     const int nb = min(col0 / 128 + lane, p.nblocks - 1);
-    s_src = SB + nb * p.sb_nb_stride;
+    s_voff = (uint32_t)nb * p.sb_nb_stride * 4;
     s_dst = T::SB_OFF;
   }
-  const int s_kb_stride = wave < BM / 64 ? p.sa_kb_stride : p.sb_kb_stride;
+  const uint32_t s_kb_bytes = (uint32_t)(a_scale_wave ? p.sa_kb_stride : p.sb_kb_stride) * 4;
 
   // ---- this wave's output block --------------------------------------------------------------
   const int i0 = (wave % WM) * T::WTM;
@@ -234,88 +272,111 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
 #pragma unroll
     for (int jg = 0; jg < T::JG; ++jg) acc[ig][jg] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto issue_loads = [&](int kb) {
+  // Load i of the LOADS per wave and K block: a slabs, then b slabs, then the scales.
+  // A zero-size resource: loads through it touch no memory and write zeros into LDS. The
+  // pipeline uses it for the blocks past the end of K, so every iteration issues the same loads.
+  const __amdgpu_buffer_rsrc_t rNone = make_rsrc(A, 0);
+
+  // Load i of the LOADS per wave for K block kb (a slabs, then b slabs, then the scales) into
+  // stage kb % STAGES; `live` false sends it through rNone.
+  auto issue_load = [&](int kb, int i, bool live) {
     uint8_t* sA = smem + (kb % STAGES) * T::STAGE_BYTES;
-    uint8_t* sB = sA + T::A_BYTES;
     const uint32_t koff = (uint32_t)kb * KBLK;
+    if (i < T::A_LOADS) {
+      load_lds_16(live ? rA : rNone, sA + (wave * T::A_LOADS + i) * 1024, a_off[i], koff);
+    } else if (i < T::A_LOADS + T::B_LOADS) {
+      const int q = i - T::A_LOADS;
+      load_lds_16(live ? rB : rNone, sA + T::A_BYTES + (wave * T::B_LOADS + q) * 1024, b_off[q], koff);
+    } else {
+      load_lds_4(live ? rS : rNone, sA + s_dst, s_voff, (uint32_t)kb * s_kb_bytes);
+    }
+  };
+  auto issue_loads = [&](int kb, bool live) {
 #pragma unroll
-    for (int q = 0; q < T::A_LOADS; ++q) load_lds_16(A + a_off[q] + koff, sA + (wave * T::A_LOADS + q) * 1024);
+    for (int i = 0; i < T::LOADS; ++i) issue_load(kb, i, live);
+  };
+
+  // One K block of this wave's MFMAs and promotions, with the loads of block kb_load (when
+  // WITH_LOADS) spread over the column groups so that no wave stalls on a burst of memory
+  // instructions before its first MFMA.
+  auto compute = [&](int kb, int kb_load, bool load_live) {
+    const uint8_t* sA = smem + (kb % STAGES) * T::STAGE_BYTES;
+    const uint8_t* sB = sA + T::A_BYTES;
+    const float* sSA = reinterpret_cast<const float*>(sA + T::SA_OFF);
+    const float sbv = reinterpret_cast<const float*>(sA + T::SB_OFF)[(col0 + j0) / 128 - col0 / 128];
+    float s[T::IG];
 #pragma unroll
-    for (int q = 0; q < T::B_LOADS; ++q) load_lds_16(B + b_off[q] + koff, sB + (wave * T::B_LOADS + q) * 1024);
-    load_lds_4(s_src + kb * s_kb_stride, sA + s_dst);
+    for (int ig = 0; ig < T::IG; ++ig) s[ig] = sSA[i0 + ig * 16 + fr] * sbv;
+    // Software pipeline over the wave's column groups: the MFMAs of group jg are issued while the
+    // FMAs that promote group jg-1 retire, and the b fragment of group jg+1 is read from LDS
+    // meanwhile, so the matrix core never waits on a VALU read of its own result.
+    i32x8 af[T::IG];
+#pragma unroll
+    for (int ig = 0; ig < T::IG; ++ig) af[ig] = load_frag(sA, i0 + ig * 16 + fr, lane);
+    i32x8 bcur = load_frag(sB, j0 + fr, lane);
+    f32x4 pend[T::IG];
+#pragma unroll
+    for (int jg = 0; jg < T::JG; ++jg) {
+#pragma unroll
+      for (int i = load_first(jg); i < load_first(jg + 1); ++i) issue_load(kb_load, i, load_live);
+      i32x8 bnext;
+      if (jg + 1 < T::JG) bnext = load_frag(sB, j0 + (jg + 1) * 16 + fr, lane);
+      f32x4 prod[T::IG];
+#pragma unroll
+      for (int ig = 0; ig < T::IG; ++ig)
+        prod[ig] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            bcur, af[ig], f32x4{0.f, 0.f, 0.f, 0.f}, FMT_E4M3, FMT_E4M3, 0, E8M0_ONE, 0, E8M0_ONE);
+      if (jg > 0) {
+#pragma unroll
+        for (int ig = 0; ig < T::IG; ++ig)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[ig][jg - 1][r] = __builtin_fmaf(pend[ig][r], s[ig], acc[ig][jg - 1][r]);
+      }
+#pragma unroll
+      for (int ig = 0; ig < T::IG; ++ig) pend[ig] = prod[ig];
+      if (jg + 1 < T::JG) bcur = bnext;
+    }
+#pragma unroll
+    for (int ig = 0; ig < T::IG; ++ig)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[ig][T::JG - 1][r] = __builtin_fmaf(pend[ig][r], s[ig], acc[ig][T::JG - 1][r]);
+    // Issue order for the block above: scales, a fragments and the first b fragment; then per
+    // column group its share of the next block's loads, its next b fragment, and
+    // (one MFMA, four VALU) x IG; then the last group's promotion.
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * T::IG + 2 + T::IG + 1, 0);
+#pragma unroll
+    for (int jg = 0; jg < T::JG; ++jg) {
+      sched_vmem_group(load_first(jg + 1) - load_first(jg));
+      if (jg + 1 < T::JG) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+#pragma unroll
+      for (int ig = 0; ig < T::IG; ++ig) {
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_VALU, 4, 0);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(SG_VALU, 4 * T::IG, 0);
   };
 
   // Pipeline: K block kb (slabs and scales) lives in stage kb % STAGES. Iteration kb waits until
   // its own loads, issued STAGES-1 iterations earlier, have landed -- with three stages the loads of
   // kb+1 stay in flight -- synchronises the workgroup (which also retires every read of the stage
-  // about to be refilled), issues the loads of kb+STAGES-1 and computes. No load in the loop
-  // targets a register, so nothing else makes the wave wait on memory.
+  // about to be refilled), then computes while issuing the loads of kb+STAGES-1. No load in the
+  // loop targets a register, so nothing else makes the wave wait on memory.
   const int KB = p.kblocks;
-  if (KB > 0) issue_loads(0);
-  if (STAGES == 3 && KB > 1) issue_loads(1);
+  if (KB > 0) issue_loads(0, true);
+  if (STAGES == 3 && KB > 0) issue_loads(1, KB > 1);
 
   for (int kb = 0; kb < KB; ++kb) {
-    if (STAGES == 3 && kb + 1 < KB)
-      wait_vmcnt<T::LOADS>();  // the newest group in flight is the loads of kb+1
-    else
-      wait_vmcnt<0>();
+    // the newest group in flight is the loads of block kb+1 (three stages) or of kb (two)
+    wait_vmcnt<STAGES == 3 ? T::LOADS : 0>();
     lds_pipeline_barrier();
-    if (kb + STAGES - 1 < KB) issue_loads(kb + STAGES - 1);
-    if (wave_live) {
-      const uint8_t* sA = smem + (kb % STAGES) * T::STAGE_BYTES;
-      const uint8_t* sB = sA + T::A_BYTES;
-      const float* sSA = reinterpret_cast<const float*>(sA + T::SA_OFF);
-      const float sbv = reinterpret_cast<const float*>(sA + T::SB_OFF)[(col0 + j0) / 128 - col0 / 128];
-      float s[T::IG];
-#pragma unroll
-      for (int ig = 0; ig < T::IG; ++ig) s[ig] = sSA[i0 + ig * 16 + fr] * sbv;
-      // Software pipeline over the wave's column groups: the MFMAs of group jg are issued while
-      // the FMAs that promote group jg-1 retire, and the b fragment of group jg+1 is read from LDS
-      // meanwhile, so the matrix core never waits on a VALU read of its own result.
-      i32x8 af[T::IG];
-#pragma unroll
-      for (int ig = 0; ig < T::IG; ++ig) af[ig] = load_frag(sA, i0 + ig * 16 + fr, lane);
-      i32x8 bcur = load_frag(sB, j0 + fr, lane);
-      f32x4 pend[T::IG];
-#pragma unroll
-      for (int jg = 0; jg < T::JG; ++jg) {
-        i32x8 bnext;
-        if (jg + 1 < T::JG) bnext = load_frag(sB, j0 + (jg + 1) * 16 + fr, lane);
-        f32x4 prod[T::IG];
-#pragma unroll
-        for (int ig = 0; ig < T::IG; ++ig)
-          prod[ig] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              bcur, af[ig], f32x4{0.f, 0.f, 0.f, 0.f}, FMT_E4M3, FMT_E4M3, 0, E8M0_ONE, 0, E8M0_ONE);
-        if (jg > 0) {
-#pragma unroll
-          for (int ig = 0; ig < T::IG; ++ig)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[ig][jg - 1][r] = __builtin_fmaf(pend[ig][r], s[ig], acc[ig][jg - 1][r]);
-        }
-#pragma unroll
-        for (int ig = 0; ig < T::IG; ++ig) pend[ig] = prod[ig];
-        if (jg + 1 < T::JG) bcur = bnext;
-      }
-#pragma unroll
-      for (int ig = 0; ig < T::IG; ++ig)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[ig][T::JG - 1][r] = __builtin_fmaf(pend[ig][r], s[ig], acc[ig][T::JG - 1][r]);
-      // Issue order for the block above: the a fragments and the first b fragment, then per
-      // column group its next b fragment followed by (one MFMA, four VALU) x IG, then the last
-      // group's promotion.
-      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * T::IG + 2 + T::IG + 1, 0);
-#pragma unroll
-      for (int jg = 0; jg < T::JG; ++jg) {
-        if (jg + 1 < T::JG) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
-#pragma unroll
-        for (int ig = 0; ig < T::IG; ++ig) {
-          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(SG_VALU, 4, 0);
-        }
-      }
-      __builtin_amdgcn_sched_group_barrier(SG_VALU, 4 * T::IG, 0);
-    }
+    const int kb_load = kb + STAGES - 1;
+    if (wave_live)
+      compute(kb, kb_load, kb_load < KB);
+    else
+      issue_loads(kb_load, kb_load < KB);
   }
+  wait_vmcnt<0>();  // the zero-fill loads of the last iterations
 
   // ---- epilogue: BF16 round-to-nearest-even, 8-byte stores of valid rows ---------------------
   if (!wave_live) return;
