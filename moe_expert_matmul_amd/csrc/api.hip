@@ -142,15 +142,12 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 }  // namespace
 
 int fp8g::tile_override() {
-  static const int value = [] {
-    const char* e = std::getenv("FP8G_TILE");
-    if (!e) return -1;
-    if (!std::strcmp(e, "256x256")) return (int)TILE_256x256;
-    if (!std::strcmp(e, "128x256")) return (int)TILE_128x256;
-    if (!std::strcmp(e, "256x128")) return (int)TILE_256x128;
-    return -1;
-  }();
-  return value;
+  const char* e = std::getenv("FP8G_TILE");
+  if (!e) return -1;
+  if (!std::strcmp(e, "256x256")) return (int)TILE_256x256;
+  if (!std::strcmp(e, "128x256")) return (int)TILE_128x256;
+  if (!std::strcmp(e, "256x128")) return (int)TILE_256x128;
+  return -1;
 }
 
 extern "C" {

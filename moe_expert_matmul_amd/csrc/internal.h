@@ -39,7 +39,8 @@ enum TileConfig : int {
 };
 
 // Tile configuration forced through the FP8G_TILE environment variable ("256x256", "128x256",
-// "256x128"), read once; -1 when unset. For tuning only: results never depend on the tile.
+// "256x128"), read at every call; -1 when unset. For tuning and for the tests that check that
+// results never depend on the tile. The contiguous form always uses 128-row tiles.
 int tile_override();
 
 int tile_rows(TileConfig cfg);

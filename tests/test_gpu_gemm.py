@@ -5,6 +5,8 @@ the full workload sizes (4096x4096x7168 plain, 32 Zipf-sized experts, 16 masked 
 sampled rows and column blocks, computed by the oracle one sample at a time.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -55,6 +57,25 @@ def test_mn_major_scales_give_bitwise_identical_output(m, n, k):
     k_out = host(_plain_call(d, "K"))
     mn_out = host(_plain_call(d, "MN"))
     assert np.array_equal(k_out, mn_out)
+
+
+@pytest.mark.parametrize("form", ["plain", "masked"])
+def test_results_do_not_depend_on_the_tile_configuration(form):
+    say("tile invariance", form)
+    outs = []
+    try:
+        for tile in ("256x256", "128x256", "256x128"):
+            os.environ["FP8G_TILE"] = tile
+            if form == "plain":
+                d = workloads.plain(300, 640, 1024, seed=21, device=DEV)
+                outs.append(host(_plain_call(d)))
+            else:
+                d = workloads.masked(3, 256, 384, 512, 128, seed=22, device=DEV,
+                                     masked_m=np.array([256, 130, 5], np.int32))
+                outs.append(host(_masked_call(d)))
+    finally:
+        os.environ.pop("FP8G_TILE", None)
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
 
 
 def test_plain_full_size_sampled_rows():
