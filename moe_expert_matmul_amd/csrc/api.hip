@@ -147,6 +147,7 @@ int fp8g::tile_override() {
   if (!std::strcmp(e, "256x256")) return (int)TILE_256x256;
   if (!std::strcmp(e, "128x256")) return (int)TILE_128x256;
   if (!std::strcmp(e, "256x128")) return (int)TILE_256x128;
+  if (!std::strcmp(e, "128x128")) return (int)TILE_128x128;
   return -1;
 }
 
@@ -222,7 +223,8 @@ fp8g_status_t fp8_group_gemm_contiguous(const void* a, const void* b, const floa
     p.b_group_stride = n * k;
     p.sb_group_stride = (n / 128) * (k / 128);
     set_scale_strides(p, scale_major, m);
-    const fp8g::TileConfig cfg = fp8g::TILE_128x256;  // one expert per 128-row tile
+    fp8g::TileConfig cfg = fp8g::TILE_128x256;  // one expert per 128-row tile
+    if (fp8g::tile_override() == fp8g::TILE_128x128) cfg = fp8g::TILE_128x128;
     p.tiles_m = (int32_t)(m / 128);
     p.tiles_n = (int32_t)ceil_div(n, fp8g::tile_cols(cfg));
     p.group_m = p.tiles_m;  // row tiles of one column tile run together and share b in L2

@@ -49,6 +49,11 @@ constexpr int SG_MFMA = 0x008;
 constexpr int SG_DS_READ = 0x100;
 constexpr int SG_VMEM = 0x010;
 
+// The next stage's loads are issued over the first LOAD_GROUPS column groups of a K block, and
+// each column group reads the b fragment of the group BPRE ahead of it.
+constexpr int LOAD_GROUPS = 4;
+constexpr int BPRE = 2;
+
 template <int BM, int BN, int WM, int WN, int STAGES>
 struct Tile {
   static constexpr int NWAVES = WM * WN;
@@ -70,7 +75,8 @@ struct Tile {
   static_assert(BM % (SLAB_ROWS * NWAVES) == 0 && BN % (SLAB_ROWS * NWAVES) == 0, "slabs");
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "16x16 MFMA blocks");
   static_assert(128 % WTN == 0, "a wave's columns must sit in one 128-wide b-scale block");
-  static_assert(STAGES == 2 || STAGES == 3, "two or three LDS stages");
+  static_assert(STAGES >= 2 && STAGES <= 4, "two to four LDS stages");
+  static_assert((STAGES - 2) * LOADS < 64, "vmcnt range");
   static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
 };
 
@@ -174,7 +180,8 @@ __global__ void __launch_bounds__(WM * WN * 64)
 gemm_fp8_groupwise_kernel(const GemmParams p) {
   using T = Tile<BM, BN, WM, WN, STAGES>;
   // first of the loads issued during column group jg (the LOADS loads spread over JG groups)
-  constexpr auto load_first = [](int jg) { return (jg * T::LOADS + T::JG - 1) / T::JG; };
+  constexpr int LG = T::JG < LOAD_GROUPS ? T::JG : LOAD_GROUPS;
+  constexpr auto load_first = [](int jg) { return ((jg < LG ? jg : LG) * T::LOADS + LG - 1) / LG; };
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * T::STAGE_BYTES];
 
   const int lane = threadIdx.x & 63;
@@ -261,9 +268,18 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   const uint32_t s_kb_bytes = (uint32_t)(a_scale_wave ? p.sa_kb_stride : p.sb_kb_stride) * 4;
 
   // ---- this wave's output block --------------------------------------------------------------
-  const int i0 = (wave % WM) * T::WTM;
-  const int j0 = (wave / WM) * T::WTN;
-  const bool wave_live = (row0 + i0 < row_end) && (col0 + j0 < p.n);
+  // Waves are numbered row-major over the WM x WN wave grid. Waves are dealt to the CU's 4 SIMDs
+  // round-robin, so the waves of one row block sit on different SIMDs and a tile whose valid rows
+  // cover only its first row blocks still spreads its work over all SIMDs.
+  const int i0 = (wave / WN) * T::WTM;
+  const int j0 = (wave % WN) * T::WTN;
+  bool wave_live = (row0 + i0 < row_end) && (col0 + j0 < p.n);
+  // In the contiguous form a wave none of whose rows belongs to the tile's expert holds padding
+  // only (one m_indices entry per lane, WTM == 64).
+  if (MODE == MODE_CONTIG) {
+    static_assert(T::WTM == 64, "one lane per wave row");
+    wave_live = wave_live && __ballot(p.rowinfo[row0 + i0 + lane] == bsel) != 0;
+  }
   const int fr = lane & 15;
 
   f32x4 acc[T::IG][T::JG];
@@ -296,9 +312,12 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     for (int i = 0; i < T::LOADS; ++i) issue_load(kb, i, live);
   };
 
-  // One K block of this wave's MFMAs and promotions, with the loads of block kb_load (when
-  // WITH_LOADS) spread over the column groups so that no wave stalls on a burst of memory
-  // instructions before its first MFMA.
+  // One K block of this wave's MFMAs and promotions, in explicit issue order. The body is cut into
+  // regions by full scheduling barriers: a prologue that reads the block's scales, the a fragments
+  // and the first BPRE b fragments, then one region per column group jg that issues its share of
+  // the next block's loads, reads the b fragment of group jg+BPRE, and alternates one MFMA of
+  // group jg with the four promotion FMAs of group jg-1, so the matrix core never waits on a VALU
+  // read of its own result and no LDS read is hoisted far ahead of its use.
   auto compute = [&](int kb, int kb_load, bool load_live) {
     const uint8_t* sA = smem + (kb % STAGES) * T::STAGE_BYTES;
     const uint8_t* sB = sA + T::A_BYTES;
@@ -307,54 +326,43 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     float s[T::IG];
 #pragma unroll
     for (int ig = 0; ig < T::IG; ++ig) s[ig] = sSA[i0 + ig * 16 + fr] * sbv;
-    // Software pipeline over the wave's column groups: the MFMAs of group jg are issued while the
-    // FMAs that promote group jg-1 retire, and the b fragment of group jg+1 is read from LDS
-    // meanwhile, so the matrix core never waits on a VALU read of its own result.
     i32x8 af[T::IG];
 #pragma unroll
     for (int ig = 0; ig < T::IG; ++ig) af[ig] = load_frag(sA, i0 + ig * 16 + fr, lane);
-    i32x8 bcur = load_frag(sB, j0 + fr, lane);
-    f32x4 pend[T::IG];
+    i32x8 bq[T::JG];
+#pragma unroll
+    for (int jg = 0; jg < BPRE && jg < T::JG; ++jg) bq[jg] = load_frag(sB, j0 + jg * 16 + fr, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 prod[T::JG][T::IG];
 #pragma unroll
     for (int jg = 0; jg < T::JG; ++jg) {
 #pragma unroll
       for (int i = load_first(jg); i < load_first(jg + 1); ++i) issue_load(kb_load, i, load_live);
-      i32x8 bnext;
-      if (jg + 1 < T::JG) bnext = load_frag(sB, j0 + (jg + 1) * 16 + fr, lane);
-      f32x4 prod[T::IG];
+      if (jg + BPRE < T::JG) bq[jg + BPRE] = load_frag(sB, j0 + (jg + BPRE) * 16 + fr, lane);
+      __builtin_amdgcn_s_setprio(1);  // favour the wave that is issuing MFMAs
 #pragma unroll
-      for (int ig = 0; ig < T::IG; ++ig)
-        prod[ig] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            bcur, af[ig], f32x4{0.f, 0.f, 0.f, 0.f}, FMT_E4M3, FMT_E4M3, 0, E8M0_ONE, 0, E8M0_ONE);
-      if (jg > 0) {
+      for (int ig = 0; ig < T::IG; ++ig) {
+        prod[jg][ig] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            bq[jg], af[ig], f32x4{0.f, 0.f, 0.f, 0.f}, FMT_E4M3, FMT_E4M3, 0, E8M0_ONE, 0, E8M0_ONE);
+        if (jg > 0) {
 #pragma unroll
-        for (int ig = 0; ig < T::IG; ++ig)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[ig][jg - 1][r] = __builtin_fmaf(pend[ig][r], s[ig], acc[ig][jg - 1][r]);
+          for (int r = 0; r < 4; ++r) acc[ig][jg - 1][r] = __builtin_fmaf(prod[jg - 1][ig][r], s[ig], acc[ig][jg - 1][r]);
+        }
       }
+      sched_vmem_group(load_first(jg + 1) - load_first(jg));
+      if (jg + BPRE < T::JG) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
 #pragma unroll
-      for (int ig = 0; ig < T::IG; ++ig) pend[ig] = prod[ig];
-      if (jg + 1 < T::JG) bcur = bnext;
+      for (int ig = 0; ig < T::IG; ++ig) {
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+        if (jg > 0) __builtin_amdgcn_sched_group_barrier(SG_VALU, 4, 0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int ig = 0; ig < T::IG; ++ig)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[ig][T::JG - 1][r] = __builtin_fmaf(pend[ig][r], s[ig], acc[ig][T::JG - 1][r]);
-    // Issue order for the block above: scales, a fragments and the first b fragment; then per
-    // column group its share of the next block's loads, its next b fragment, and
-    // (one MFMA, four VALU) x IG; then the last group's promotion.
-    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * T::IG + 2 + T::IG + 1, 0);
-#pragma unroll
-    for (int jg = 0; jg < T::JG; ++jg) {
-      sched_vmem_group(load_first(jg + 1) - load_first(jg));
-      if (jg + 1 < T::JG) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
-#pragma unroll
-      for (int ig = 0; ig < T::IG; ++ig) {
-        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(SG_VALU, 4, 0);
-      }
-    }
-    __builtin_amdgcn_sched_group_barrier(SG_VALU, 4 * T::IG, 0);
+      for (int r = 0; r < 4; ++r) acc[ig][T::JG - 1][r] = __builtin_fmaf(prod[T::JG - 1][ig][r], s[ig], acc[ig][T::JG - 1][r]);
   };
 
   // Pipeline: K block kb (slabs and scales) lives in stage kb % STAGES. Iteration kb waits until
@@ -363,12 +371,14 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   // about to be refilled), then computes while issuing the loads of kb+STAGES-1. No load in the
   // loop targets a register, so nothing else makes the wave wait on memory.
   const int KB = p.kblocks;
-  if (KB > 0) issue_loads(0, true);
-  if (STAGES == 3 && KB > 0) issue_loads(1, KB > 1);
+  if (KB > 0) {
+#pragma unroll
+    for (int b = 0; b < STAGES - 1; ++b) issue_loads(b, b < KB);
+  }
 
   for (int kb = 0; kb < KB; ++kb) {
-    // the newest group in flight is the loads of block kb+1 (three stages) or of kb (two)
-    wait_vmcnt<STAGES == 3 ? T::LOADS : 0>();
+    // block kb has landed once at most the loads of blocks kb+1 .. kb+STAGES-2 are in flight
+    wait_vmcnt<(STAGES - 2) * T::LOADS>();
     lds_pipeline_barrier();
     const int kb_load = kb + STAGES - 1;
     if (wave_live)
@@ -424,14 +434,15 @@ hipError_t launch_cfg(GemmMode mode, const GemmParams& p, int grid, hipStream_t 
 
 using namespace kernels;
 
-int tile_rows(TileConfig cfg) { return cfg == TILE_128x256 ? 128 : 256; }
-int tile_cols(TileConfig cfg) { return cfg == TILE_256x128 ? 128 : 256; }
+int tile_rows(TileConfig cfg) { return (cfg == TILE_128x256 || cfg == TILE_128x128) ? 128 : 256; }
+int tile_cols(TileConfig cfg) { return (cfg == TILE_256x128 || cfg == TILE_128x128) ? 128 : 256; }
 
 hipError_t launch_gemm(GemmMode mode, TileConfig cfg, GemmParams p, int grid, hipStream_t stream) {
   switch (cfg) {
     case TILE_256x256: return launch_cfg<256, 256, 4, 2, 2>(mode, p, grid, stream);
     case TILE_128x256: return launch_cfg<128, 256, 2, 4, 3>(mode, p, grid, stream);
     case TILE_256x128: return launch_cfg<256, 128, 4, 2, 3>(mode, p, grid, stream);
+    case TILE_128x128: return launch_cfg<128, 128, 2, 2, 4>(mode, p, grid, stream);
   }
   return hipErrorInvalidValue;
 }

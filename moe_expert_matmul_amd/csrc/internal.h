@@ -36,10 +36,11 @@ enum TileConfig : int {
   TILE_256x256 = 0,  // 8 waves as 4 (rows) x 2 (cols), 64x128 per wave, 2 LDS stages
   TILE_128x256 = 1,  // 8 waves as 2 x 4, 64x64 per wave, 3 LDS stages
   TILE_256x128 = 2,  // 8 waves as 4 x 2, 64x64 per wave, 3 LDS stages
+  TILE_128x128 = 3,  // 4 waves as 2 x 2, 64x64 per wave, 4 LDS stages (weight streaming)
 };
 
 // Tile configuration forced through the FP8G_TILE environment variable ("256x256", "128x256",
-// "256x128"), read at every call; -1 when unset. For tuning and for the tests that check that
+// "256x128", "128x128"), read at every call; -1 when unset. For tuning and for the tests that check that
 // results never depend on the tile. The contiguous form always uses 128-row tiles.
 int tile_override();
 
