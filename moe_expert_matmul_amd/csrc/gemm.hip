@@ -201,24 +201,47 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   const int col0 = tn * BN;
 
   int row_end = p.m;  // rows at or beyond row_end hold no valid output
-  int bsel = 0;       // group of b / b_scale
+  // Experts (b groups) of the passes this tile runs. Plain: one pass on b. Masked: one pass on
+  // group g. Contiguous: each 128-row half of the tile holds one expert (plus padding); a tile
+  // whose halves hold the same expert runs one pass, otherwise one pass per half, each with only
+  // that half's waves live.
+  int pass_expert[2] = {0, 0};
+  int pass_half_mask[2] = {3, 3};  // bit h: waves of 128-row half h take part
+  int npass = 1;
   if (MODE == MODE_MASKED) {
     const int mm = max(0, min(p.rowinfo[g], p.m));
     if (row0 >= mm) return;
     row_end = mm;
-    bsel = g;
+    pass_expert[0] = g;
   } else if (MODE == MODE_CONTIG) {
-    int e = -1;
-    for (int r = lane; r < BM; r += 64) e = max(e, p.rowinfo[row0 + r]);
-    e = wave_max(e);
-    if (e < 0 || e >= p.num_groups) return;  // padding-only tile
-    bsel = e;
+    constexpr int HALVES = BM / 128;
+    int ex[HALVES];
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h) {
+      int e = -1;
+      if (row0 + h * 128 < p.m)
+        for (int r = lane; r < 128; r += 64) e = max(e, p.rowinfo[row0 + h * 128 + r]);
+      e = wave_max(e);
+      ex[h] = (e >= 0 && e < p.num_groups) ? e : -1;  // -1: padding only
+    }
+    npass = 0;
+    if (HALVES == 2 && ex[0] >= 0 && ex[0] == ex[1]) {
+      pass_expert[0] = ex[0];
+      npass = 1;
+    } else {
+#pragma unroll
+      for (int h = 0; h < HALVES; ++h)
+        if (ex[h] >= 0) {
+          pass_expert[npass] = ex[h];
+          pass_half_mask[npass] = 1 << h;
+          ++npass;
+        }
+    }
+    if (npass == 0) return;  // padding-only tile
   }
 
   const uint8_t* A = p.a + (int64_t)g * p.a_group_stride;
-  const uint8_t* B = p.b + (int64_t)bsel * p.b_group_stride;
   const float* SA = p.sa + (int64_t)g * p.sa_group_stride;
-  const float* SB = p.sb + (int64_t)bsel * p.sb_group_stride;
 
   // ---- HBM -> LDS load assignment ----------------------------------------------------------
   // Slab s (1 KB) holds tile rows [8s, 8s+8); lane l fills its chunk l, i.e. tile row
@@ -243,17 +266,14 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     b_off[q] = (uint32_t)r * (uint32_t)p.k + lchunk * 16;
   }
 
-  // Buffer resources of this tile's operands (per group for the grouped forms).
-  const uint32_t a_bytes = (uint32_t)p.m * (uint32_t)p.k;
+  // Buffer resources of this tile's operands (per group for the grouped forms; b's per pass).
   const uint32_t b_bytes = (uint32_t)p.n * (uint32_t)p.k;
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(A, a_bytes);
-  const __amdgpu_buffer_rsrc_t rB = make_rsrc(B, b_bytes);
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(A, (uint32_t)p.m * (uint32_t)p.k);
+  __amdgpu_buffer_rsrc_t rB, rS;
 
   // Scales of a K block travel with its slabs: waves 0 .. BM/64-1 each fetch 64 of a's row
   // scales, every other wave fetches b's BN/128 block scales (identical data to the same place).
   const bool a_scale_wave = wave < BM / 64;
-  const __amdgpu_buffer_rsrc_t rS =
-      a_scale_wave ? make_rsrc(SA, (uint32_t)p.m * p.kblocks * 4) : make_rsrc(SB, (uint32_t)p.nblocks * p.kblocks * 4);
   uint32_t s_voff;
   int s_dst;
   if (a_scale_wave) {
@@ -273,20 +293,11 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   // cover only its first row blocks still spreads its work over all SIMDs.
   const int i0 = (wave / WN) * T::WTM;
   const int j0 = (wave % WN) * T::WTN;
-  bool wave_live = (row0 + i0 < row_end) && (col0 + j0 < p.n);
-  // In the contiguous form a wave none of whose rows belongs to the tile's expert holds padding
-  // only (one m_indices entry per lane, WTM == 64).
-  if (MODE == MODE_CONTIG) {
-    static_assert(T::WTM == 64, "one lane per wave row");
-    wave_live = wave_live && __ballot(p.rowinfo[row0 + i0 + lane] == bsel) != 0;
-  }
   const int fr = lane & 15;
+  bool wave_live = false;
+  int bsel = 0;
 
   f32x4 acc[T::IG][T::JG];
-#pragma unroll
-  for (int ig = 0; ig < T::IG; ++ig)
-#pragma unroll
-    for (int jg = 0; jg < T::JG; ++jg) acc[ig][jg] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Load i of the LOADS per wave and K block: a slabs, then b slabs, then the scales.
   // A zero-size resource: loads through it touch no memory and write zeros into LDS. The
@@ -371,6 +382,26 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   // about to be refilled), then computes while issuing the loads of kb+STAGES-1. No load in the
   // loop targets a register, so nothing else makes the wave wait on memory.
   const int KB = p.kblocks;
+  for (int ps = 0; ps < npass; ++ps) {
+  bsel = pass_expert[ps];
+  {
+    const uint8_t* B = p.b + (int64_t)bsel * p.b_group_stride;
+    const float* SB = p.sb + (int64_t)bsel * p.sb_group_stride;
+    rB = make_rsrc(B, b_bytes);
+    rS = a_scale_wave ? make_rsrc(SA, (uint32_t)p.m * p.kblocks * 4) : make_rsrc(SB, (uint32_t)p.nblocks * p.kblocks * 4);
+  }
+  wave_live = (row0 + i0 < row_end) && (col0 + j0 < p.n) && ((pass_half_mask[ps] >> (i0 / 128)) & 1);
+  // In the contiguous form a wave none of whose rows belongs to the pass's expert holds padding
+  // (or the other half's rows) only: one m_indices entry per lane, WTM == 64.
+  if (MODE == MODE_CONTIG) {
+    static_assert(T::WTM == 64, "one lane per wave row");
+    wave_live = wave_live && __ballot(p.rowinfo[row0 + i0 + lane] == bsel) != 0;
+  }
+#pragma unroll
+  for (int ig = 0; ig < T::IG; ++ig)
+#pragma unroll
+    for (int jg = 0; jg < T::JG; ++jg) acc[ig][jg] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (ps > 0) lds_pipeline_barrier();  // every wave is done with the previous pass's stages
   if (KB > 0) {
 #pragma unroll
     for (int b = 0; b < STAGES - 1; ++b) issue_loads(b, b < KB);
@@ -389,7 +420,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   wait_vmcnt<0>();  // the zero-fill loads of the last iterations
 
   // ---- epilogue: BF16 round-to-nearest-even, 8-byte stores of valid rows ---------------------
-  if (!wave_live) return;
+  if (wave_live) {
   uint16_t* O = p.out + (int64_t)g * p.out_group_stride;
   const int jl = (lane >> 4) * 4;
 #pragma unroll
@@ -411,6 +442,8 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
       *reinterpret_cast<uint2*>(orow + j) = v;
     }
   }
+  }  // wave_live
+  }  // passes
 }
 
 template <int BM, int BN, int WM, int WN, int STAGES>

@@ -59,7 +59,7 @@ def test_mn_major_scales_give_bitwise_identical_output(m, n, k):
     assert np.array_equal(k_out, mn_out)
 
 
-@pytest.mark.parametrize("form", ["plain", "masked"])
+@pytest.mark.parametrize("form", ["plain", "masked", "contiguous"])
 def test_results_do_not_depend_on_the_tile_configuration(form):
     say("tile invariance", form)
     outs = []
@@ -69,10 +69,14 @@ def test_results_do_not_depend_on_the_tile_configuration(form):
             if form == "plain":
                 d = workloads.plain(300, 640, 1024, seed=21, device=DEV)
                 outs.append(host(_plain_call(d)))
-            else:
+            elif form == "masked":
                 d = workloads.masked(3, 256, 384, 512, 128, seed=22, device=DEV,
                                      masked_m=np.array([256, 130, 5], np.int32))
                 outs.append(host(_masked_call(d)))
+            else:
+                # 256-row tiles whose halves hold one expert, two experts, an expert and padding
+                d = workloads.contiguous(5, n=384, k=512, seed=23, device=DEV, counts=[200, 100, 0, 129, 40])
+                outs.append(host(_contig_call(d)))
     finally:
         os.environ.pop("FP8G_TILE", None)
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
