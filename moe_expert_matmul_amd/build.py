@@ -24,6 +24,8 @@ SOURCES = ["api.hip", "gemm.hip", "moe.hip"]
 
 ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source extra compiler flags (none at present).
+SOURCE_FLAGS: dict = {}
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-command-line-argument",
                 "-fvisibility=hidden",
                 "-I", os.path.join(ROOT, "include")]
@@ -54,7 +56,8 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        jobs.append([hipcc, *COMMON_FLAGS, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([hipcc, *COMMON_FLAGS, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+                     "-o", obj])
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as ex:
         for lines in ex.map(_run, jobs):
             if verbose:

@@ -28,26 +28,10 @@
 // drops tiles at or beyond masked_m[g]; the contiguous form reads the tile's 128 m_indices and drops
 // tiles that hold only padding. Rows that are not valid are still computed when they share a wave
 // with valid rows (each output row depends only on its own a row and scale) but never stored.
-#include "internal.h"
+#include "gemm_common.h"
 
 namespace fp8g {
 namespace kernels {
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-constexpr int KBLK = 128;         // K-block width = bytes of one row per K block
-constexpr int SLAB_ROWS = 8;      // rows filled by one wave-wide 16-byte-per-lane LDS load
-constexpr int E8M0_ONE = 127;     // 2^0 as an E8M0 block scale
-constexpr int FMT_E4M3 = 0;       // f8f6f4 operand format code of FP8 E4M3
-
-// Instruction classes of __builtin_amdgcn_sched_group_barrier.
-constexpr int SG_VALU = 0x002;
-constexpr int SG_MFMA = 0x008;
-constexpr int SG_DS_READ = 0x100;
-constexpr int SG_VMEM = 0x010;
 
 // The next stage's loads are issued over the first LOAD_GROUPS column groups of a K block, and
 // each column group reads the b fragment of the group BPRE ahead of it.
@@ -79,101 +63,6 @@ struct Tile {
   static_assert((STAGES - 2) * LOADS < 64, "vmcnt range");
   static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
 };
-
-// A sched_group_barrier of n (0..12) memory instructions; n folds to a constant after unrolling.
-__device__ __forceinline__ void sched_vmem_group(int n) {
-  switch (n) {
-    case 1: __builtin_amdgcn_sched_group_barrier(SG_VMEM, 1, 0); break;
-    case 2: __builtin_amdgcn_sched_group_barrier(SG_VMEM, 2, 0); break;
-    case 3: __builtin_amdgcn_sched_group_barrier(SG_VMEM, 3, 0); break;
-    case 4: __builtin_amdgcn_sched_group_barrier(SG_VMEM, 4, 0); break;
-    case 5: __builtin_amdgcn_sched_group_barrier(SG_VMEM, 5, 0); break;
-    case 6: __builtin_amdgcn_sched_group_barrier(SG_VMEM, 6, 0); break;
-    case 7: __builtin_amdgcn_sched_group_barrier(SG_VMEM, 7, 0); break;
-    case 8: __builtin_amdgcn_sched_group_barrier(SG_VMEM, 8, 0); break;
-    case 9: __builtin_amdgcn_sched_group_barrier(SG_VMEM, 9, 0); break;
-    case 10: __builtin_amdgcn_sched_group_barrier(SG_VMEM, 10, 0); break;
-    case 11: __builtin_amdgcn_sched_group_barrier(SG_VMEM, 11, 0); break;
-    case 12: __builtin_amdgcn_sched_group_barrier(SG_VMEM, 12, 0); break;
-    default: break;
-  }
-}
-
-// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt in bits 3:0 and
-// 15:14, expcnt 6:4, lgkmcnt 11:8). A real S_WAITCNT, so the compiler's own wait insertion sees it.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier for the LDS pipeline. The LDS reads of this wave are retired first
-// (lgkmcnt(0)) so a stage can be refilled after it; the slab loads' visibility is handled by the
-// caller's vmcnt wait. Unlike __syncthreads() it carries no release fence, which would drain every
-// load in flight, including the ones meant to stay in flight across the barrier. The empty asm
-// statements keep the compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_pipeline_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maximum
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Buffer resource (base, byte size) for the loads below; word 3 is the gfx9 raw-buffer format.
-// Accesses past `bytes` read zero instead of faulting.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 ... lds): lane l reads
-// byte offset voff + soff and writes bytes [16l, 16l+16) of the 1 KB block at the wave-uniform
-// address `lds`. soff is a scalar, so the per-lane offset is the only vector register used.
-__device__ __forceinline__ void load_lds_16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, 0);
-}
-
-// 4 bytes per lane into LDS: lane l writes bytes [4l, 4l+4) at `lds`.
-__device__ __forceinline__ void load_lds_4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, voff, soff, 0, 0);
-}
-
-__device__ __forceinline__ int wave_max(int v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
-  return v;
-}
-
-// Renumber workgroups so that ids t and t+1 run on the same XCD (dispatch is round-robin).
-__device__ __forceinline__ int xcd_local_order(int t, int total) {
-  const int full = total & ~7;
-  return t < full ? (t & 7) * (full >> 3) + (t >> 3) : t;
-}
-
-__device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int group_m, int& tm, int& tn) {
-  const int per_group = group_m * tiles_n;
-  const int gid = t / per_group;
-  const int first = gid * group_m;
-  const int gm = min(tiles_m - first, group_m);
-  const int r = t - gid * per_group;
-  tm = first + r % gm;
-  tn = r / gm;
-}
-
-// Physical 16-byte chunk of logical chunk c in tile row r is c ^ swizzle(r).
-__device__ __forceinline__ int swizzle(int row) { return (row >> 1) & 7; }
-
-// One 16x128 FP8 operand fragment: lane l supplies row (l & 15) of the 16-row group and the 16-byte
-// chunks g and g+4 of the K block, g = l >> 4. Both operands use the same K assignment, which is
-// all the matrix core needs for a dot product over the block. (Lane groups reading chunks g and
-// g+4 keep each ds_read_b128 free of bank conflicts; chunks 2g and 2g+1 measured half the rate.)
-__device__ __forceinline__ i32x8 load_frag(const uint8_t* slab, int row, int lane) {
-  const uint8_t* rp = slab + row * KBLK;
-  const int c0 = lane >> 4;
-  const int sw = swizzle(row);
-  const i32x4 lo = *reinterpret_cast<const i32x4*>(rp + ((c0 ^ sw) << 4));
-  const i32x4 hi = *reinterpret_cast<const i32x4*>(rp + (((c0 + 4) ^ sw) << 4));
-  return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-}
 
 template <int BM, int BN, int WM, int WN, int STAGES, int MODE>
 __global__ void __launch_bounds__(WM * WN * 64)
@@ -468,7 +357,9 @@ hipError_t launch_cfg(GemmMode mode, const GemmParams& p, int grid, hipStream_t 
 using namespace kernels;
 
 int tile_rows(TileConfig cfg) { return (cfg == TILE_128x256 || cfg == TILE_128x128) ? 128 : 256; }
-int tile_cols(TileConfig cfg) { return (cfg == TILE_256x128 || cfg == TILE_128x128) ? 128 : 256; }
+int tile_cols(TileConfig cfg) {
+  return (cfg == TILE_256x128 || cfg == TILE_128x128) ? 128 : 256;
+}
 
 hipError_t launch_gemm(GemmMode mode, TileConfig cfg, GemmParams p, int grid, hipStream_t stream) {
   switch (cfg) {
