@@ -223,11 +223,13 @@ fp8g_status_t fp8_group_gemm_contiguous(const void* a, const void* b, const floa
     p.b_group_stride = n * k;
     p.sb_group_stride = (n / 128) * (k / 128);
     set_scale_strides(p, scale_major, m);
-    // 128x256 tiles (one expert each) measured faster than 256-row tiles here: a 256-row tile
-    // whose halves hold different experts runs one pass per expert, which costs two tile times.
+    // 128x256 tiles: the weights stream from HBM here, and the three-stage pipeline of that tile
+    // hides the latency better than the two stages of the 256x256 tile. With 256-row tiles a tile
+    // whose two 128-row halves hold different experts is split into two workgroups, so the grid
+    // counts two entries per 256-row tile.
     fp8g::TileConfig cfg = fp8g::TILE_128x256;
     if (fp8g::tile_override() >= 0) cfg = (fp8g::TileConfig)fp8g::tile_override();
-    p.tiles_m = (int32_t)ceil_div(m, fp8g::tile_rows(cfg));
+    p.tiles_m = (int32_t)(ceil_div(m, fp8g::tile_rows(cfg)) * (fp8g::tile_rows(cfg) / 128));
     p.tiles_n = (int32_t)ceil_div(n, fp8g::tile_cols(cfg));
     p.group_m = p.tiles_m;  // row tiles of one column tile run together and share b in L2
     const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;

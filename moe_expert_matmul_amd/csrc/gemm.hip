@@ -86,22 +86,29 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   }
   int tm, tn;
   raster(t, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+  // Contiguous form with 256-row tiles: the grid holds two entries per row tile (tm = 2 * tile +
+  // half), so a tile whose two 128-row halves belong to different experts runs as two workgroups.
+  int half = 0;
+  if (MODE == MODE_CONTIG && BM == 256) {
+    half = tm & 1;
+    tm >>= 1;
+  }
   const int row0 = tm * BM;
   const int col0 = tn * BN;
 
   int row_end = p.m;  // rows at or beyond row_end hold no valid output
-  // Experts (b groups) of the passes this tile runs. Plain: one pass on b. Masked: one pass on
-  // group g. Contiguous: each 128-row half of the tile holds one expert (plus padding); a tile
-  // whose halves hold the same expert runs one pass, otherwise one pass per half, each with only
-  // that half's waves live.
-  int pass_expert[2] = {0, 0};
-  int pass_half_mask[2] = {3, 3};  // bit h: waves of 128-row half h take part
-  int npass = 1;
+  // The b group this workgroup multiplies with, and the 128-row halves of the tile it covers
+  // (bit h: waves of half h take part). Plain: b, whole tile. Masked: group g, whole tile.
+  // Contiguous: each 128-row half holds one expert (plus padding); the first entry of a tile whose
+  // halves hold the same expert covers the whole tile and the second exits, otherwise each entry
+  // covers its own half (or exits when that half is padding only).
+  int bsel = 0;
+  int half_mask = 3;
   if (MODE == MODE_MASKED) {
     const int mm = max(0, min(p.rowinfo[g], p.m));
     if (row0 >= mm) return;
     row_end = mm;
-    pass_expert[0] = g;
+    bsel = g;
   } else if (MODE == MODE_CONTIG) {
     constexpr int HALVES = BM / 128;
     int ex[HALVES];
@@ -110,23 +117,17 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
       int e = -1;
       if (row0 + h * 128 < p.m)
         for (int r = lane; r < 128; r += 64) e = max(e, p.rowinfo[row0 + h * 128 + r]);
-      e = wave_max(e);
-      ex[h] = (e >= 0 && e < p.num_groups) ? e : -1;  // -1: padding only
+      e = __builtin_amdgcn_readfirstlane(wave_max(e));  // uniform: keeps b's resource scalar
+      ex[h] = (e >= 0 && e < p.num_groups) ? e : -1;       // -1: padding only
     }
-    npass = 0;
-    if (HALVES == 2 && ex[0] >= 0 && ex[0] == ex[1]) {
-      pass_expert[0] = ex[0];
-      npass = 1;
+    if (HALVES == 2 && ex[0] >= 0 && ex[0] == ex[HALVES - 1]) {
+      if (half == 1) return;
+      bsel = ex[0];
     } else {
-#pragma unroll
-      for (int h = 0; h < HALVES; ++h)
-        if (ex[h] >= 0) {
-          pass_expert[npass] = ex[h];
-          pass_half_mask[npass] = 1 << h;
-          ++npass;
-        }
+      if (ex[half] < 0) return;
+      bsel = ex[half];
+      half_mask = 1 << half;
     }
-    if (npass == 0) return;  // padding-only tile
   }
 
   const uint8_t* A = p.a + (int64_t)g * p.a_group_stride;
@@ -155,10 +156,11 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     b_off[q] = (uint32_t)r * (uint32_t)p.k + lchunk * 16;
   }
 
-  // Buffer resources of this tile's operands (per group for the grouped forms; b's per pass).
-  const uint32_t b_bytes = (uint32_t)p.n * (uint32_t)p.k;
+  // Buffer resources of this tile's operands (per group for the grouped forms).
+  const uint8_t* B = p.b + (int64_t)bsel * p.b_group_stride;
+  const float* SB = p.sb + (int64_t)bsel * p.sb_group_stride;
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(A, (uint32_t)p.m * (uint32_t)p.k);
-  __amdgpu_buffer_rsrc_t rB, rS;
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(B, (uint32_t)p.n * (uint32_t)p.k);
 
   // Scales of a K block travel with its slabs: waves 0 .. BM/64-1 each fetch 64 of a's row
   // scales, every other wave fetches b's BN/128 block scales (identical data to the same place).
@@ -175,6 +177,8 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     s_dst = T::SB_OFF;
   }
   const uint32_t s_kb_bytes = (uint32_t)(a_scale_wave ? p.sa_kb_stride : p.sb_kb_stride) * 4;
+  const __amdgpu_buffer_rsrc_t rS = a_scale_wave ? make_rsrc(SA, (uint32_t)p.m * p.kblocks * 4)
+                                                 : make_rsrc(SB, (uint32_t)p.nblocks * p.kblocks * 4);
 
   // ---- this wave's output block --------------------------------------------------------------
   // Waves are numbered row-major over the WM x WN wave grid. Waves are dealt to the CU's 4 SIMDs
@@ -183,8 +187,13 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   const int i0 = (wave / WN) * T::WTM;
   const int j0 = (wave % WN) * T::WTN;
   const int fr = lane & 15;
-  bool wave_live = false;
-  int bsel = 0;
+  bool wave_live = (row0 + i0 < row_end) && (col0 + j0 < p.n) && ((half_mask >> (i0 / 128)) & 1);
+  // In the contiguous form a wave none of whose rows belongs to the expert holds padding (or the
+  // other half's rows) only: one m_indices entry per lane, WTM == 64.
+  if (MODE == MODE_CONTIG) {
+    static_assert(T::WTM == 64, "one lane per wave row");
+    wave_live = wave_live && __ballot(p.rowinfo[row0 + i0 + lane] == bsel) != 0;
+  }
 
   f32x4 acc[T::IG][T::JG];
 
@@ -199,7 +208,9 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     uint8_t* sA = smem + (kb % STAGES) * T::STAGE_BYTES;
     const uint32_t koff = (uint32_t)kb * KBLK;
     if (i < T::A_LOADS) {
-      load_lds_16(live ? rA : rNone, sA + (wave * T::A_LOADS + i) * 1024, a_off[i], koff);
+      // slabs of a 128-row half this workgroup does not cover are not fetched
+      const int half_live = __builtin_amdgcn_readfirstlane((half_mask >> ((wave * T::A_LOADS + i) * SLAB_ROWS / 128)) & 1);
+      load_lds_16(live && half_live ? rA : rNone, sA + (wave * T::A_LOADS + i) * 1024, a_off[i], koff);
     } else if (i < T::A_LOADS + T::B_LOADS) {
       const int q = i - T::A_LOADS;
       load_lds_16(live ? rB : rNone, sA + T::A_BYTES + (wave * T::B_LOADS + q) * 1024, b_off[q], koff);
@@ -271,26 +282,10 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   // about to be refilled), then computes while issuing the loads of kb+STAGES-1. No load in the
   // loop targets a register, so nothing else makes the wave wait on memory.
   const int KB = p.kblocks;
-  for (int ps = 0; ps < npass; ++ps) {
-  bsel = pass_expert[ps];
-  {
-    const uint8_t* B = p.b + (int64_t)bsel * p.b_group_stride;
-    const float* SB = p.sb + (int64_t)bsel * p.sb_group_stride;
-    rB = make_rsrc(B, b_bytes);
-    rS = a_scale_wave ? make_rsrc(SA, (uint32_t)p.m * p.kblocks * 4) : make_rsrc(SB, (uint32_t)p.nblocks * p.kblocks * 4);
-  }
-  wave_live = (row0 + i0 < row_end) && (col0 + j0 < p.n) && ((pass_half_mask[ps] >> (i0 / 128)) & 1);
-  // In the contiguous form a wave none of whose rows belongs to the pass's expert holds padding
-  // (or the other half's rows) only: one m_indices entry per lane, WTM == 64.
-  if (MODE == MODE_CONTIG) {
-    static_assert(T::WTM == 64, "one lane per wave row");
-    wave_live = wave_live && __ballot(p.rowinfo[row0 + i0 + lane] == bsel) != 0;
-  }
 #pragma unroll
   for (int ig = 0; ig < T::IG; ++ig)
 #pragma unroll
     for (int jg = 0; jg < T::JG; ++jg) acc[ig][jg] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (ps > 0) lds_pipeline_barrier();  // every wave is done with the previous pass's stages
   if (KB > 0) {
 #pragma unroll
     for (int b = 0; b < STAGES - 1; ++b) issue_loads(b, b < KB);
@@ -332,7 +327,6 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     }
   }
   }  // wave_live
-  }  // passes
 }
 
 template <int BM, int BN, int WM, int WN, int STAGES>
