@@ -231,7 +231,10 @@ fp8g_status_t fp8_group_gemm_contiguous(const void* a, const void* b, const floa
     if (fp8g::tile_override() >= 0) cfg = (fp8g::TileConfig)fp8g::tile_override();
     p.tiles_m = (int32_t)(ceil_div(m, fp8g::tile_rows(cfg)) * (fp8g::tile_rows(cfg) / 128));
     p.tiles_n = (int32_t)ceil_div(n, fp8g::tile_cols(cfg));
-    p.group_m = p.tiles_m;  // row tiles of one column tile run together and share b in L2
+    // 128-row tiles: the row tiles of one column tile run together and share b's slab in L2.
+    // 256-row tiles: the column tiles of one row tile run together and share a's rows in L2 (each
+    // expert's weights are streamed once either way); measured 1.8x faster for them.
+    p.group_m = fp8g::tile_rows(cfg) == 256 ? 1 : p.tiles_m;
     const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
     require(grid <= kInt32Max, "too many tiles");
     check_hip(fp8g::launch_gemm(fp8g::MODE_CONTIG, cfg, p, (int)grid, (hipStream_t)stream),
