@@ -7,6 +7,8 @@
 // division, so that its decisions are reproducible; a block of zeros gets scale 1. Each 128-wide
 // block is handled by 16 lanes holding 8 consecutive elements (16-byte loads), and its amax is a
 // 16-lane butterfly reduction.
+#include <algorithm>
+
 #include "internal.h"
 
 namespace fp8g {
@@ -53,108 +55,110 @@ __device__ __forceinline__ float team16_max(float v) {
   return v;
 }
 
-__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
-  return x;
-}
-
-__device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
-}
-
-constexpr int kPermThreads = 256;
-constexpr int kPermPerThread = 8;
+constexpr int kPermThreads = 1024;  // 16 waves
+constexpr int kPermWaves = kPermThreads / 64;
 constexpr int kMaxExperts = 1024;
+constexpr int kExpertBits = 10;      // ids below kMaxExperts
+constexpr int kPermBatch = 8;        // groups of 64 ids loaded together
 
-// One workgroup per expert. Every workgroup histograms all entries (the ids are small and stay in
-// L2), takes its region offset as the sum of the 128-padded counts of the experts before it, and
-// then compacts its own entries in ascending entry order with a block-wide exclusive scan, so the
-// result does not depend on scheduling.
+// Lanes of this wave whose (valid) id equals this lane's: one ballot per id bit.
+__device__ __forceinline__ uint64_t match_id(int id, bool valid) {
+  uint64_t m = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < kExpertBits; ++b) {
+    const uint64_t ones = __ballot(valid && ((id >> b) & 1));
+    m &= ((id >> b) & 1) ? ones : ~ones;
+  }
+  return m;
+}
+
+// Stable counting sort of the (token, slot) entries by expert. Workgroup c places the entries of
+// chunk c (kPermThreads entries, one group of 64 per wave). Every workgroup counts all entries per
+// expert -- in total, and before its chunk -- which gives the experts' 128-padded regions and the
+// chunk's first row inside each; within the chunk, the lanes holding the same expert find each
+// other with bit ballots (match_id), so an entry's row is its region start, plus the entries of
+// its expert in earlier chunks, in earlier groups of the chunk, and in earlier lanes. Entries keep
+// their order inside an expert, whatever the schedule. Workgroup 0 also writes the padding rows.
 __global__ void __launch_bounds__(kPermThreads)
 moe_permutation_kernel(const int32_t* __restrict__ ids, int entries, int top_k, int num_experts,
                        int m_alloc, int32_t* __restrict__ m_indices, int32_t* __restrict__ src_token,
                        int32_t* __restrict__ row_of_entry) {
-  __shared__ int hist[kMaxExperts];
-  __shared__ int wave_part[kPermThreads / 64];
-  const int e = blockIdx.x;
+  __shared__ int total_cnt[kMaxExperts];               // entries per expert
+  __shared__ int before_cnt[kMaxExperts];              // ... in earlier chunks
+  __shared__ int group_cnt[kPermWaves][kMaxExperts];   // ... in each group of this chunk
+  __shared__ int region[kMaxExperts + 1];              // first row of each region; [E]: rows used
+  __shared__ int scan_part[kPermWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t lanes_below = (1ull << lane) - 1;
+  const int chunk_begin = blockIdx.x * kPermThreads;
 
-  for (int i = tid; i < num_experts; i += kPermThreads) hist[i] = 0;
-  __syncthreads();
-  for (int i = tid; i < entries; i += kPermThreads) {
-    const int v = ids[i];
-    if (v >= 0 && v < num_experts) atomicAdd(&hist[v], 1);
-  }
+  for (int i = tid; i < kMaxExperts; i += kPermThreads) total_cnt[i] = before_cnt[i] = 0;
+  for (int i = tid; i < kPermWaves * kMaxExperts; i += kPermThreads) (&group_cnt[0][0])[i] = 0;
   __syncthreads();
 
-  int part = 0;
-  for (int i = tid; i < e; i += kPermThreads) part += (hist[i] + 127) & ~127;
-  part = wave_sum(part);
-  if (lane == 0) wave_part[wave] = part;
-  __syncthreads();
-  int offset = 0;
+  // counts over all entries, kPermBatch groups of 64 per wave at a time so that the loads overlap
+  for (int g0 = wave * 64 * kPermBatch; g0 < entries; g0 += kPermThreads * kPermBatch) {
+    int idv[kPermBatch];
 #pragma unroll
-  for (int w = 0; w < kPermThreads / 64; ++w) offset += wave_part[w];
-  const int count = hist[e];
+    for (int u = 0; u < kPermBatch; ++u) {
+      const int idx = g0 + u * 64 + lane;
+      idv[u] = idx < entries ? ids[idx] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kPermBatch; ++u) {
+      const int id = idv[u];
+      const bool valid = id >= 0 && id < num_experts;
+      const uint64_t same = match_id(id, valid);
+      if (valid && (same >> lane) == 1) {  // the last lane holding this expert adds for all of them
+        atomicAdd(&total_cnt[id], __popcll(same));
+        if (g0 + u * 64 < chunk_begin) atomicAdd(&before_cnt[id], __popcll(same));  // groups never straddle
+      }
+    }
+  }
+  const int idx = chunk_begin + wave * 64 + lane;  // this lane's entry of the chunk
+  const int id = idx < entries ? ids[idx] : -1;
+  const bool valid = id >= 0 && id < num_experts;
+  const uint64_t same = match_id(id, valid);
+  if (valid && (same >> lane) == 1) group_cnt[wave][id] = __popcll(same);
+  __syncthreads();
+
+  // regions: block-wide exclusive scan of the 128-padded counts, one thread per expert
+  const int count = tid < num_experts ? total_cnt[tid] : 0;
   const int padded = (count + 127) & ~127;
-  __syncthreads();  // wave_part is reused below
-
-  int base = 0;
-  for (int c0 = 0; c0 < entries; c0 += kPermThreads * kPermPerThread) {
-    const int first = c0 + tid * kPermPerThread;
-    int flags = 0, mine = 0;
+  int incl = padded;
 #pragma unroll
-    for (int u = 0; u < kPermPerThread; ++u) {
-      const int idx = first + u;
-      if (idx < entries && ids[idx] == e) {
-        flags |= 1 << u;
-        ++mine;
-      }
-    }
-    const int incl = wave_inclusive_scan(mine, lane);
-    if (lane == 63) wave_part[wave] = incl;
-    __syncthreads();
-    int before = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < kPermThreads / 64; ++w) {
-      before += w < wave ? wave_part[w] : 0;
-      total += wave_part[w];
-    }
-    int row = offset + base + before + incl - mine;
-#pragma unroll
-    for (int u = 0; u < kPermPerThread; ++u) {
-      if (flags & (1 << u)) {
-        const int idx = first + u;
-        m_indices[row] = e;
-        src_token[row] = idx / top_k;
-        row_of_entry[idx] = row;
-        ++row;
-      }
-    }
-    base += total;
-    __syncthreads();
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
   }
-
-  for (int r = offset + count + tid; r < offset + padded; r += kPermThreads) {
-    m_indices[r] = -1;
-    src_token[r] = -1;
-  }
-  if (e == num_experts - 1) {
-    for (int r = offset + padded + tid; r < m_alloc; r += kPermThreads) {
+  if (lane == 63) scan_part[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += scan_part[w];
+  const int start = before + incl - padded;
+  if (tid < num_experts) region[tid] = start;
+  if (tid == kPermThreads - 1) region[num_experts] = before + incl;
+  if (blockIdx.x == 0 && tid < num_experts) {
+    for (int r = start + count; r < start + padded; ++r) {  // the region's padding rows
       m_indices[r] = -1;
       src_token[r] = -1;
     }
   }
-  if (e == 0) {
-    for (int i = tid; i < entries; i += kPermThreads) {
-      const int v = ids[i];
-      if (v < 0 || v >= num_experts) row_of_entry[i] = -1;
+  __syncthreads();
+
+  if (valid) {
+    int row = region[id] + before_cnt[id] + __popcll(same & lanes_below);
+    for (int w = 0; w < wave; ++w) row += group_cnt[w][id];
+    m_indices[row] = id;
+    src_token[row] = idx / top_k;
+    row_of_entry[idx] = row;
+  } else if (idx < entries) {
+    row_of_entry[idx] = -1;
+  }
+  if (blockIdx.x == 0) {
+    for (int r = region[num_experts] + tid; r < m_alloc; r += kPermThreads) {  // rows past every region
+      m_indices[r] = -1;
+      src_token[r] = -1;
     }
   }
 }
@@ -244,7 +248,8 @@ hipError_t launch_moe_build_permutation(const int32_t* topk_ids, int num_tokens,
                                         int num_experts, int m_alloc, int32_t* m_indices,
                                         int32_t* src_token, int32_t* row_of_entry,
                                         hipStream_t stream) {
-  hipLaunchKernelGGL(moe_permutation_kernel, dim3(num_experts), dim3(kPermThreads), 0, stream, topk_ids,
+  const int chunks = std::max(1, (num_tokens * top_k + kPermThreads - 1) / kPermThreads);
+  hipLaunchKernelGGL(moe_permutation_kernel, dim3(chunks), dim3(kPermThreads), 0, stream, topk_ids,
                      num_tokens * top_k, top_k, num_experts, m_alloc, m_indices, src_token, row_of_entry);
   return hipGetLastError();
 }

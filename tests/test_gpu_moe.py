@@ -89,6 +89,29 @@ def _stagewise(d, out, ws, p, rows, token_sample, col_blocks_fc1, col_blocks_fc2
     return flips
 
 
+@pytest.mark.parametrize("num_tokens,top_k,num_experts", [(1, 1, 1), (5, 3, 7), (777, 1, 1024), (4096, 8, 64),
+                                                            (20000, 6, 129)])
+def test_permutation_matches_oracle(num_tokens, top_k, num_experts):
+    """The permutation alone: odd sizes, one expert, 1024 experts, ~5% unrouted (-1 or out-of-range) ids."""
+    say("permutation", num_tokens, top_k, num_experts)
+    rng = np.random.default_rng(num_tokens + 7 * num_experts)
+    ids = np.stack([rng.permutation(num_experts)[:top_k] if top_k <= num_experts else
+                    rng.integers(0, num_experts, top_k) for _ in range(num_tokens)]).astype(np.int32)
+    drop = rng.random(ids.shape) < 0.05
+    ids[drop] = rng.choice(np.array([-1, num_experts, num_experts + 5], np.int32), int(drop.sum()))
+    m_alloc = fp8g.default_m_alloc(num_tokens, top_k, num_experts) + 256
+    dev_ids = torch.from_numpy(ids).to(DEV)
+    m_indices = torch.full((m_alloc,), 12345, dtype=torch.int32, device=DEV)
+    src_token = torch.full((m_alloc,), 12345, dtype=torch.int32, device=DEV)
+    row_of_entry = torch.full((num_tokens, top_k), 12345, dtype=torch.int32, device=DEV)
+    fp8g.moe_build_permutation(dev_ids, num_experts, m_indices, src_token, row_of_entry)
+    torch.cuda.synchronize()
+    p = omoe.build_permutation(ids, num_experts, m_alloc)
+    assert np.array_equal(host(m_indices), p["m_indices"])
+    assert np.array_equal(host(src_token), p["src_token"])
+    assert np.array_equal(host(row_of_entry).reshape(-1), p["row_of_entry"].reshape(-1))
+
+
 def test_moe_small_all_stages_and_end_to_end():
     say("moe small T=256 H=512 E=8 k=2 I=256")
     d = workloads.moe(num_tokens=256, hidden=512, num_experts=8, top_k=2, inter=256, seed=1, device=DEV)
