@@ -102,6 +102,27 @@ FP8G_API fp8g_status_t fp8_group_gemm_contiguous(const void* a, const void* b, c
                                         int32_t gran_k, void* stream);
 
 /*
+ * Contiguous grouped form with gathered rows of a: row r of the product reads row a_rows[r] of a
+ * (and of a_scale), i.e. out[r] = a[a_rows[r]] @ b[m_indices[r]].T for every r with
+ * m_indices[r] >= 0. This is the contiguous form of the MATE FlashInfer-API page (section "GEMM")
+ * applied to the permuted token rows of the expert FFN (flashinfer-rs README, section "API
+ * Example: Fused MoE FP8 (cudarc)"), without materialising the permuted copy of the tokens.
+ *   a          (a_rows_total, k) E4M3; a_scale (a_rows_total, k/128) K-major or
+ *              (k/128, a_rows_total) MN-major
+ *   a_rows     (m,) int32 device array; entries of rows with m_indices[r] >= 0 must lie in
+ *              [0, a_rows_total) (other rows are never stored; an out-of-range entry there reads
+ *              row 0)
+ *   everything else as fp8_group_gemm_contiguous.
+ */
+FP8G_API fp8g_status_t fp8_group_gemm_contiguous_gather(const void* a, const float* a_scale,
+                                               int64_t a_rows_total, const int32_t* a_rows,
+                                               const void* b, const float* b_scale,
+                                               const int32_t* m_indices, void* out, int64_t m,
+                                               int64_t n, int64_t k, int64_t num_groups,
+                                               int32_t scale_major, int32_t gran_m, int32_t gran_n,
+                                               int32_t gran_k, void* stream);
+
+/*
  * Masked batched form: out[g, :masked_m[g]] = a[g, :masked_m[g]] @ b[g].T.
  * MATE FlashInfer-API page, section "GEMM", batch_deepgemm_fp8_nt_groupwise.
  *   a          (num_groups, max_m, k)  E4M3
@@ -151,7 +172,9 @@ FP8G_API fp8g_status_t fp8_moe_build_permutation(const int32_t* topk_ids, int64_
  *     a_out[r][c*128 + t] = E4M3_RNE(x[s][c*128 + t] / scale[r][c])
  *   x        (num_tokens, hidden) BF16
  *   a_out    (m_alloc, hidden) E4M3 out; a_scale_out (m_alloc, hidden/128) FP32 out (K-major)
- * Rows with src_token = -1 are not written.
+ * Rows with src_token = -1 are not written. src_token may be null: row r then quantises token r
+ * (m_alloc <= num_tokens), which, with fp8_group_gemm_contiguous_gather, replaces the gathered
+ * copy of the tokens by one quantised copy read through src_token.
  */
 FP8G_API fp8g_status_t fp8_moe_gather_quant(const void* x, const int32_t* src_token, int64_t num_tokens,
                                    int64_t hidden, int64_t m_alloc, void* a_out,

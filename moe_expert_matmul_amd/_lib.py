@@ -26,6 +26,8 @@ SIGNATURES = {
     "fp8_gemm_nt_groupwise": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P], _I32),
     "fp8_group_gemm_contiguous": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P],
                                   _I32),
+    "fp8_group_gemm_contiguous_gather": ([_P, _P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32,
+                                          _I32, _P], _I32),
     "fp8_batch_gemm_masked": ([_P, _P, _P, _P, _P, _I64, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P],
                               _I32),
     "fp8_moe_build_permutation": ([_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P], _I32),

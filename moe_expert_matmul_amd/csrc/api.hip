@@ -180,6 +180,7 @@ fp8g_status_t fp8_gemm_nt_groupwise(const void* a, const void* b, const float* a
     p.kblocks = (int32_t)(k / 128);
     p.nblocks = (int32_t)(n / 128);
     p.num_groups = 1;
+    p.a_src_rows = (int32_t)m;
     set_scale_strides(p, scale_major, m);
     fp8g::TileConfig cfg = m > 128 ? fp8g::TILE_256x256 : fp8g::TILE_128x256;
     if (fp8g::tile_override() >= 0) cfg = (fp8g::TileConfig)fp8g::tile_override();
@@ -192,53 +193,87 @@ fp8g_status_t fp8_gemm_nt_groupwise(const void* a, const void* b, const float* a
   });
 }
 
+}  // extern "C"
+
+namespace {
+
+// The contiguous form, with a's rows read directly (a_rows null, a_src_rows == m) or gathered.
+void group_gemm_contiguous(const void* a, const float* a_scale, int64_t a_src_rows, const int32_t* a_rows,
+                           const void* b, const float* b_scale, const int32_t* m_indices, void* out, int64_t m,
+                           int64_t n, int64_t k, int64_t num_groups, int32_t scale_major, int32_t gran_m,
+                           int32_t gran_n, int32_t gran_k, void* stream, const char* what) {
+  check_gemm_dims(m, n, k);
+  check_gemm_dims(a_src_rows, n, k);
+  require(num_groups >= 0 && num_groups <= kInt32Max, "num_groups must be in [0, 2^31)");
+  require(m % 128 == 0, "m (%lld) must be a multiple of 128 (128-row-aligned expert regions)", (long long)m);
+  check_scale_major(scale_major);
+  check_granularity(gran_m, gran_n, gran_k);
+  if (m == 0 || n == 0 || num_groups == 0) return;
+  check_operands(a, b, a_scale, b_scale, out, k);
+  require(m_indices != nullptr && aligned(m_indices, 4), "m_indices must be non-null and 4-byte aligned");
+  require(a_rows == nullptr || aligned(a_rows, 4), "a_rows must be 4-byte aligned");
+  require(k == 0 || a_src_rows > 0, "a must have at least one row");
+  check_device();
+  fp8g::GemmParams p{};
+  p.a = static_cast<const uint8_t*>(a);
+  p.b = static_cast<const uint8_t*>(b);
+  p.sa = a_scale;
+  p.sb = b_scale;
+  p.out = static_cast<uint16_t*>(out);
+  p.rowinfo = m_indices;
+  p.a_rows = a_rows;
+  p.a_src_rows = (int32_t)a_src_rows;
+  p.m = (int32_t)m;
+  p.n = (int32_t)n;
+  p.k = (int32_t)k;
+  p.kblocks = (int32_t)(k / 128);
+  p.nblocks = (int32_t)(n / 128);
+  p.num_groups = (int32_t)num_groups;
+  p.b_group_stride = n * k;
+  p.sb_group_stride = (n / 128) * (k / 128);
+  set_scale_strides(p, scale_major, a_src_rows);
+  // 128x256 tiles: the weights stream from HBM here, and the three-stage pipeline of that tile
+  // hides the latency better than the two stages of the 256x256 tile. With 256-row tiles a tile
+  // whose two 128-row halves hold different experts is split into two workgroups, so the grid
+  // counts two entries per 256-row tile.
+  fp8g::TileConfig cfg = fp8g::TILE_128x256;
+  if (fp8g::tile_override() >= 0) cfg = (fp8g::TileConfig)fp8g::tile_override();
+  p.tiles_m = (int32_t)(ceil_div(m, fp8g::tile_rows(cfg)) * (fp8g::tile_rows(cfg) / 128));
+  p.tiles_n = (int32_t)ceil_div(n, fp8g::tile_cols(cfg));
+  // 128-row tiles: the row tiles of one column tile run together and share b's slab in L2.
+  // 256-row tiles: the column tiles of one row tile run together and share a's rows in L2 (each
+  // expert's weights are streamed once either way); measured 1.8x faster for them.
+  p.group_m = fp8g::tile_rows(cfg) == 256 ? 1 : p.tiles_m;
+  const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
+  require(grid <= kInt32Max, "too many tiles");
+  check_hip(fp8g::launch_gemm(fp8g::MODE_CONTIG, cfg, p, (int)grid, (hipStream_t)stream), what);
+}
+
+}  // namespace
+
+extern "C" {
+
 fp8g_status_t fp8_group_gemm_contiguous(const void* a, const void* b, const float* a_scale,
                                         const float* b_scale, const int32_t* m_indices, void* out,
                                         int64_t m, int64_t n, int64_t k, int64_t num_groups,
                                         int32_t scale_major, int32_t gran_m, int32_t gran_n,
                                         int32_t gran_k, void* stream) {
   return guarded([&] {
-    check_gemm_dims(m, n, k);
-    require(num_groups >= 0 && num_groups <= kInt32Max, "num_groups must be in [0, 2^31)");
-    require(m % 128 == 0, "m (%lld) must be a multiple of 128 (128-row-aligned expert regions)", (long long)m);
-    check_scale_major(scale_major);
-    check_granularity(gran_m, gran_n, gran_k);
-    if (m == 0 || n == 0 || num_groups == 0) return;
-    check_operands(a, b, a_scale, b_scale, out, k);
-    require(m_indices != nullptr && aligned(m_indices, 4), "m_indices must be non-null and 4-byte aligned");
-    check_device();
-    fp8g::GemmParams p{};
-    p.a = static_cast<const uint8_t*>(a);
-    p.b = static_cast<const uint8_t*>(b);
-    p.sa = a_scale;
-    p.sb = b_scale;
-    p.out = static_cast<uint16_t*>(out);
-    p.rowinfo = m_indices;
-    p.m = (int32_t)m;
-    p.n = (int32_t)n;
-    p.k = (int32_t)k;
-    p.kblocks = (int32_t)(k / 128);
-    p.nblocks = (int32_t)(n / 128);
-    p.num_groups = (int32_t)num_groups;
-    p.b_group_stride = n * k;
-    p.sb_group_stride = (n / 128) * (k / 128);
-    set_scale_strides(p, scale_major, m);
-    // 128x256 tiles: the weights stream from HBM here, and the three-stage pipeline of that tile
-    // hides the latency better than the two stages of the 256x256 tile. With 256-row tiles a tile
-    // whose two 128-row halves hold different experts is split into two workgroups, so the grid
-    // counts two entries per 256-row tile.
-    fp8g::TileConfig cfg = fp8g::TILE_128x256;
-    if (fp8g::tile_override() >= 0) cfg = (fp8g::TileConfig)fp8g::tile_override();
-    p.tiles_m = (int32_t)(ceil_div(m, fp8g::tile_rows(cfg)) * (fp8g::tile_rows(cfg) / 128));
-    p.tiles_n = (int32_t)ceil_div(n, fp8g::tile_cols(cfg));
-    // 128-row tiles: the row tiles of one column tile run together and share b's slab in L2.
-    // 256-row tiles: the column tiles of one row tile run together and share a's rows in L2 (each
-    // expert's weights are streamed once either way); measured 1.8x faster for them.
-    p.group_m = fp8g::tile_rows(cfg) == 256 ? 1 : p.tiles_m;
-    const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
-    require(grid <= kInt32Max, "too many tiles");
-    check_hip(fp8g::launch_gemm(fp8g::MODE_CONTIG, cfg, p, (int)grid, (hipStream_t)stream),
-              "fp8_group_gemm_contiguous launch");
+    group_gemm_contiguous(a, a_scale, m, nullptr, b, b_scale, m_indices, out, m, n, k, num_groups, scale_major,
+                          gran_m, gran_n, gran_k, stream, "fp8_group_gemm_contiguous launch");
+  });
+}
+
+fp8g_status_t fp8_group_gemm_contiguous_gather(const void* a, const float* a_scale, int64_t a_rows_total,
+                                               const int32_t* a_rows, const void* b, const float* b_scale,
+                                               const int32_t* m_indices, void* out, int64_t m, int64_t n,
+                                               int64_t k, int64_t num_groups, int32_t scale_major,
+                                               int32_t gran_m, int32_t gran_n, int32_t gran_k,
+                                               void* stream) {
+  return guarded([&] {
+    require(m == 0 || a_rows != nullptr, "a_rows must be non-null");
+    group_gemm_contiguous(a, a_scale, a_rows_total, a_rows, b, b_scale, m_indices, out, m, n, k, num_groups,
+                          scale_major, gran_m, gran_n, gran_k, stream, "fp8_group_gemm_contiguous_gather launch");
   });
 }
 
@@ -273,6 +308,7 @@ fp8g_status_t fp8_batch_gemm_masked(const void* a, const void* b, const float* a
     p.a_group_stride = max_m * k;
     p.b_group_stride = n * k;
     p.sa_group_stride = max_m * (k / 128);
+    p.a_src_rows = (int32_t)max_m;
     p.sb_group_stride = (n / 128) * (k / 128);
     p.out_group_stride = max_m * n;
     set_scale_strides(p, scale_major, max_m);
@@ -322,8 +358,9 @@ fp8g_status_t fp8_moe_gather_quant(const void* x, const int32_t* src_token, int6
     require(num_tokens >= 0 && hidden >= 0 && m_alloc >= 0, "sizes must be non-negative");
     require(hidden % 128 == 0, "hidden (%lld) must be a multiple of 128", (long long)hidden);
     require(m_alloc <= kInt32Max && hidden <= kInt32Max && num_tokens <= kInt32Max, "sizes must fit in int32");
+    require(src_token != nullptr || m_alloc <= num_tokens, "without src_token, m_alloc must not exceed num_tokens");
     if (m_alloc == 0 || hidden == 0) return;
-    require(x && src_token && a_out && a_scale_out, "pointers must be non-null");
+    require(x && a_out && a_scale_out, "pointers must be non-null");
     require(aligned(x, 16) && aligned(a_out, 16) && aligned(a_scale_out, 4) && aligned(src_token, 4),
             "x and a_out must be 16-byte aligned, src_token and a_scale_out 4-byte aligned");
     check_device();

@@ -140,12 +140,19 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   // clamped to the last valid row), so the pipeline can wait on a fixed count of outstanding loads.
   const int lrow = lane >> 3;
   const int a_last = row_end - 1;
+  // The row of a (and of a_scale) that tile row r reads: r itself, or a_rows[r] when the contiguous
+  // form gathers its rows (rows whose index is out of range read row 0; they are never stored).
+  auto a_source_row = [&](int r) {
+    if (MODE != MODE_CONTIG || p.a_rows == nullptr) return r;
+    const int s = p.a_rows[r];
+    return (s >= 0 && s < p.a_src_rows) ? s : 0;
+  };
   uint32_t a_off[T::A_LOADS], b_off[T::B_LOADS];
 #pragma unroll
   for (int q = 0; q < T::A_LOADS; ++q) {
     const int slab_row = (wave * T::A_LOADS + q) * SLAB_ROWS;
     const int lchunk = (lane & 7) ^ swizzle(slab_row + lrow);
-    const int r = min(row0 + slab_row + lrow, a_last);
+    const int r = a_source_row(min(row0 + slab_row + lrow, a_last));
     a_off[q] = (uint32_t)r * (uint32_t)p.k + lchunk * 16;
   }
 #pragma unroll
@@ -159,7 +166,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   // Buffer resources of this tile's operands (per group for the grouped forms).
   const uint8_t* B = p.b + (int64_t)bsel * p.b_group_stride;
   const float* SB = p.sb + (int64_t)bsel * p.sb_group_stride;
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(A, (uint32_t)p.m * (uint32_t)p.k);
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(A, (uint32_t)p.a_src_rows * (uint32_t)p.k);
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(B, (uint32_t)p.n * (uint32_t)p.k);
 
   // Scales of a K block travel with its slabs: waves 0 .. BM/64-1 each fetch 64 of a's row
@@ -168,7 +175,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   uint32_t s_voff;
   int s_dst;
   if (a_scale_wave) {
-    const int r = min(row0 + wave * 64 + lane, p.m - 1);
+    const int r = a_source_row(min(row0 + wave * 64 + lane, p.m - 1));
     s_voff = (uint32_t)r * p.sa_row_stride * 4;
     s_dst = T::SA_OFF + wave * 256;
   } else {
@@ -177,7 +184,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     s_dst = T::SB_OFF;
   }
   const uint32_t s_kb_bytes = (uint32_t)(a_scale_wave ? p.sa_kb_stride : p.sb_kb_stride) * 4;
-  const __amdgpu_buffer_rsrc_t rS = a_scale_wave ? make_rsrc(SA, (uint32_t)p.m * p.kblocks * 4)
+  const __amdgpu_buffer_rsrc_t rS = a_scale_wave ? make_rsrc(SA, (uint32_t)p.a_src_rows * p.kblocks * 4)
                                                  : make_rsrc(SB, (uint32_t)p.nblocks * p.kblocks * 4);
 
   // ---- this wave's output block --------------------------------------------------------------

@@ -21,6 +21,8 @@ struct GemmParams {
   const float* sb;
   uint16_t* out;
   const int32_t* rowinfo;  // m_indices (CONTIG) or masked_m (MASKED)
+  const int32_t* a_rows;   // CONTIG only: row r of the product takes row a_rows[r] of a; null: r
+  int32_t a_src_rows;      // rows of a (and of a_scale) in memory
   int64_t a_group_stride, b_group_stride, sa_group_stride, sb_group_stride, out_group_stride;
   int32_t m;  // PLAIN/CONTIG: rows of a; MASKED: max_m
   int32_t n, k;

@@ -170,7 +170,7 @@ moe_gather_quant_kernel(const uint16_t* __restrict__ x, const int32_t* __restric
                         int num_tokens, int hidden, uint8_t* __restrict__ a_out,
                         float* __restrict__ a_scale_out) {
   const int row = blockIdx.x;
-  const int t = src_token[row];
+  const int t = src_token != nullptr ? src_token[row] : row;  // null: rows are the tokens themselves
   if (t < 0 || t >= num_tokens) return;
   const int nblk = hidden / 128;
   const int sub = threadIdx.x & 15;

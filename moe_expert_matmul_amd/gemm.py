@@ -94,6 +94,30 @@ def fp8_group_gemm_contiguous(a, b, a_scale, b_scale, m_indices, out, scale_majo
     return out
 
 
+def fp8_group_gemm_contiguous_gather(a, a_scale, a_rows, b, b_scale, m_indices, out, scale_major="K",
+                                     granularity=_GRAN) -> torch.Tensor:
+    """out[i] = a[a_rows[i]] @ b[m_indices[i]].T for rows with m_indices[i] >= 0 (others untouched)."""
+    dev = _require_cuda(a)
+    rows_total, k = a.shape
+    m = m_indices.shape[0]
+    groups, n, _ = b.shape
+    kb, nb = k // 128, n // 128
+    major = _major(scale_major)
+    _check(a, "a", _FP8_DTYPES, (rows_total, k), dev)
+    _check(a_scale, "a_scale", (torch.float32,), (rows_total, kb) if major == 0 else (kb, rows_total), dev)
+    _check(a_rows, "a_rows", (torch.int32,), (m,), dev)
+    _check(b, "b", _FP8_DTYPES, (groups, n, k), dev)
+    _check(b_scale, "b_scale", (torch.float32,), (groups, nb, kb) if major == 0 else (groups, kb, nb), dev)
+    _check(m_indices, "m_indices", (torch.int32,), (m,), dev)
+    _check(out, "out", (torch.bfloat16,), (m, n), dev)
+    with torch.cuda.device(dev):
+        st = _lib.load().fp8_group_gemm_contiguous_gather(_ptr(a), _ptr(a_scale), rows_total, _ptr(a_rows), _ptr(b),
+                                                          _ptr(b_scale), _ptr(m_indices), _ptr(out), m, n, k, groups,
+                                                          major, *granularity, _stream(dev))
+    _lib.check(st, "fp8_group_gemm_contiguous_gather")
+    return out
+
+
 def fp8_batch_gemm_masked(a, b, a_scale, b_scale, masked_m, expected_m, out, scale_major="K",
                           granularity=_GRAN) -> torch.Tensor:
     """out[g, :masked_m[g]] = a[g, :masked_m[g]] @ b[g].T (other rows untouched)."""

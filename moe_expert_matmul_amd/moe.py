@@ -6,7 +6,8 @@ first ``inter`` rows are the gate and the next ``inter`` the up projection, FP8 
 (E, hidden, inter), 128x128 FP32 block scales, and the top-k routing weights for the combine.
 
 Six library calls on the current stream, no host synchronisation:
-  permutation -> gather+quantise -> fc1 grouped GEMM -> SiLU-mul+quantise -> fc2 grouped GEMM -> combine
+  permutation -> quantise the tokens -> fc1 grouped GEMM reading the token rows through the
+  permutation -> SiLU-mul+quantise -> fc2 grouped GEMM -> combine
 """
 
 from __future__ import annotations
@@ -16,7 +17,7 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from .gemm import _check, _require_cuda, _stream, fp8_group_gemm_contiguous
+from .gemm import _check, _require_cuda, _stream, fp8_group_gemm_contiguous, fp8_group_gemm_contiguous_gather
 
 
 def default_m_alloc(num_tokens: int, top_k: int, num_experts: int) -> int:
@@ -32,7 +33,7 @@ class MoeWorkspace:
     m_indices: torch.Tensor
     src_token: torch.Tensor
     row_of_entry: torch.Tensor
-    a1: torch.Tensor
+    a1: torch.Tensor  # the tokens, 1x128-quantised (num_tokens rows, in token order)
     sa1: torch.Tensor
     y1: torch.Tensor
     a2: torch.Tensor
@@ -47,8 +48,8 @@ class MoeWorkspace:
             m_indices=torch.empty(m_alloc, dtype=torch.int32, **e),
             src_token=torch.empty(m_alloc, dtype=torch.int32, **e),
             row_of_entry=torch.empty((num_tokens, top_k), dtype=torch.int32, **e),
-            a1=torch.empty((m_alloc, hidden), dtype=torch.uint8, **e),
-            sa1=torch.empty((m_alloc, hidden // 128), dtype=torch.float32, **e),
+            a1=torch.empty((num_tokens, hidden), dtype=torch.uint8, **e),
+            sa1=torch.empty((num_tokens, hidden // 128), dtype=torch.float32, **e),
             y1=torch.empty((m_alloc, 2 * inter), dtype=torch.bfloat16, **e),
             a2=torch.empty((m_alloc, inter), dtype=torch.uint8, **e),
             sa2=torch.empty((m_alloc, inter // 128), dtype=torch.float32, **e),
@@ -76,16 +77,20 @@ def moe_build_permutation(topk_ids, num_experts, m_indices, src_token, row_of_en
 
 
 def moe_gather_quant(x, src_token, a_out, a_scale_out):
+    """Row r of a_out/a_scale_out: x[src_token[r]] quantised per 1x128 block (rows with -1 untouched).
+
+    With ``src_token=None`` row r quantises token r (a_out holds at most num_tokens rows)."""
     dev = _require_cuda(x)
     t, h = x.shape
-    m_alloc = src_token.shape[0]
+    m_alloc = a_out.shape[0] if src_token is None else src_token.shape[0]
     _check(x, "x", (torch.bfloat16,), (t, h), dev)
-    _check(src_token, "src_token", (torch.int32,), (m_alloc,), dev)
+    if src_token is not None:
+        _check(src_token, "src_token", (torch.int32,), (m_alloc,), dev)
     _check(a_out, "a_out", (torch.uint8, torch.float8_e4m3fn), (m_alloc, h), dev)
     _check(a_scale_out, "a_scale_out", (torch.float32,), (m_alloc, h // 128), dev)
     with torch.cuda.device(dev):
-        st = _lib.load().fp8_moe_gather_quant(x.data_ptr(), src_token.data_ptr(), t, h, m_alloc,
-                                              a_out.data_ptr(), a_scale_out.data_ptr(), _stream(dev))
+        st = _lib.load().fp8_moe_gather_quant(x.data_ptr(), None if src_token is None else src_token.data_ptr(),
+                                              t, h, m_alloc, a_out.data_ptr(), a_scale_out.data_ptr(), _stream(dev))
     _lib.check(st, "fp8_moe_gather_quant")
 
 
@@ -129,8 +134,8 @@ def moe_ffn_fp8_block_scale(x, topk_ids, topk_weights, w1, s1, w2, s2, out=None,
     if out is None:
         out = torch.empty((num_tokens, hidden), dtype=torch.bfloat16, device=x.device)
     moe_build_permutation(topk_ids, num_experts, ws.m_indices, ws.src_token, ws.row_of_entry)
-    moe_gather_quant(x, ws.src_token, ws.a1, ws.sa1)
-    fp8_group_gemm_contiguous(ws.a1, w1, ws.sa1, s1, ws.m_indices, ws.y1)
+    moe_gather_quant(x, None, ws.a1, ws.sa1)
+    fp8_group_gemm_contiguous_gather(ws.a1, ws.sa1, ws.src_token, w1, s1, ws.m_indices, ws.y1)
     moe_silu_mul_quant(ws.y1, ws.m_indices, ws.a2, ws.sa2)
     fp8_group_gemm_contiguous(ws.a2, w2, ws.sa2, s2, ws.m_indices, ws.y2)
     moe_combine(ws.y2, ws.row_of_entry, topk_weights, out)

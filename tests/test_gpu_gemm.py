@@ -317,6 +317,35 @@ def test_contiguous_mn_major_bitwise_equal():
     assert np.array_equal(host(_contig_call(d, "K")), host(_contig_call(d, "MN")))
 
 
+@pytest.mark.parametrize("major", ["K", "MN"])
+def test_contiguous_gather_equals_contiguous_on_gathered_rows(major):
+    """Rows of a read through a_rows (with -1 on padding rows) give exactly the contiguous result."""
+    counts = [130, 0, 5, 300, 1]
+    say("contiguous gather", counts, major)
+    d = workloads.contiguous(len(counts), n=384, k=512, seed=31, device=DEV, counts=counts)
+    m = d["m"]
+    rng = np.random.default_rng(31)
+    tokens = 97
+    src = rng.integers(0, tokens, m).astype(np.int32)
+    mi = host(d["m_indices"])
+    src[mi < 0] = -1
+    xa = workloads.plain(tokens, 128, 512, seed=32, device=DEV)  # token rows (a) and their scales
+    a_tok, sa_tok = xa["a"], xa["a_scale"]
+    src_d = torch.from_numpy(src).to(DEV)
+    sa_arg = sa_tok if major == "K" else sa_tok.t().contiguous()
+    out_g = sentinel_like((m, d["n"]), DEV)
+    fp8g.fp8_group_gemm_contiguous_gather(a_tok, sa_arg, src_d, d["b"], d["b_scale"] if major == "K" else
+                                          d["b_scale"].transpose(1, 2).contiguous(), d["m_indices"], out_g, major)
+    torch.cuda.synchronize()
+    g = torch.from_numpy(np.maximum(src, 0)).to(DEV).long()
+    d2 = dict(d, a=a_tok[g].contiguous(), a_scale=sa_tok[g].contiguous())
+    out_c = _contig_call(d2, major)
+    assert np.array_equal(host(out_g), host(out_c))
+    ref = _contig_ref(d2)
+    assert_within_tolerance(bf16_values(out_g), ref, "contiguous gather")
+    assert untouched(out_g)[mi < 0].all()
+
+
 def test_contiguous_full_size_sampled():
     say("contiguous full size: 32 Zipf experts, 8192 rows, n=4096, k=7168")
     d = workloads.contiguous(32, 8192, 4096, 7168, 1.1, seed=0, device=DEV)
