@@ -30,12 +30,16 @@ sys.path.insert(0, ROOT)
 FP8_DENSE_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 matrix-core peak
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_plain_4096x4096x7168.json")
-KERNEL_SOURCE = os.path.join(ROOT, "moe_expert_matmul_amd", "csrc", "gemm.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "moe_expert_matmul_amd", "csrc", f) for f in ("gemm.hip", "gemm_common.h")]
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] over the sources of the GEMM kernel (the traffic counters are tied to them)."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic():
@@ -97,7 +101,7 @@ def cpu_baseline(d, flops_per_row):
                       default=1)
     except Exception:  # threadpoolctl missing: numpy's BLAS uses every core by default
         threads = os.cpu_count()
-    rows = 192
+    rows = 2048  # about 2 s of wall time on 16 host cores
     a = workloads.to_numpy(d["a"][:rows])
     sa = workloads.to_numpy(d["a_scale"][:rows])
     b = workloads.to_numpy(d["b"])
@@ -108,7 +112,8 @@ def cpu_baseline(d, flops_per_row):
     return {"value": round(rows * flops_per_row / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"first {rows} of 4096 rows x all 4096 columns x k=7168 of the plain workload "
-                      f"({rows * flops_per_row / 1e9:.1f} GFLOP, {dt:.1f} s, float64 BLAS per 128-wide K block)"}
+                      f"({rows * flops_per_row / 1e9:.1f} GFLOP, {dt:.1f} s wall on {int(threads)} threads, "
+                      f"float64 BLAS per 128-wide K block)"}
 
 
 def other_configs(steps, warmup):
