@@ -192,6 +192,29 @@ FP8G_API fp8g_status_t fp8_moe_silu_mul_quant(const void* y, const int32_t* m_in
                                      void* stream);
 
 /*
+ * The expert FFN's fc1 and its activation in one pass: the bytes fp8_group_gemm_contiguous_gather
+ * (a_rows non-null) or fp8_group_gemm_contiguous (a_rows null) would write to y = fc1 output
+ * (BF16, gate columns then up columns) followed by fp8_moe_silu_mul_quant(y), bit for bit, without
+ * writing y (flashinfer-rs README, section "API Example: Fused MoE FP8 (cudarc)": the fused FP8
+ * MoE; the GEMM itself is the contiguous form of the MATE FlashInfer-API page, section "GEMM").
+ *   a, a_scale, a_rows_total, a_rows   as fp8_group_gemm_contiguous_gather (a_rows may be null:
+ *                                      then a has m rows)
+ *   w1          (num_experts, 2*inter, hidden) E4M3, gate rows then up rows; w1_scale FP32
+ *               (num_experts, 2*inter/128, hidden/128) K-major or (num_experts, hidden/128,
+ *               2*inter/128) MN-major (the same mode as a_scale)
+ *   m_indices   (m,) int32, 128-row-aligned expert regions, -1 padding
+ *   q_out       (m, inter) E4M3 out; q_scale_out (m, inter/128) FP32 out (K-major); rows with
+ *               m_indices < 0 are not written
+ * inter must be a multiple of 128, hidden of 128.
+ */
+FP8G_API fp8g_status_t fp8_moe_fc1_silu_quant(const void* a, const float* a_scale, int64_t a_rows_total,
+                                     const int32_t* a_rows, const void* w1, const float* w1_scale,
+                                     const int32_t* m_indices, void* q_out, float* q_scale_out,
+                                     int64_t m, int64_t inter, int64_t hidden, int64_t num_experts,
+                                     int32_t scale_major, int32_t gran_m, int32_t gran_n,
+                                     int32_t gran_k, void* stream);
+
+/*
  * out[t] = bf16( sum_s topk_weights[t][s] * y[row_of_entry[t][s]] ), summed in FP32 in slot
  * order; entries with row_of_entry = -1 contribute nothing.
  *   y             (m_alloc, hidden) BF16 (the fc2 output)

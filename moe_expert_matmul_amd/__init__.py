@@ -20,6 +20,7 @@ from .moe import (  # noqa: F401
     default_m_alloc,
     moe_build_permutation,
     moe_combine,
+    moe_fc1_silu_quant,
     moe_ffn_fp8_block_scale,
     moe_gather_quant,
     moe_silu_mul_quant,

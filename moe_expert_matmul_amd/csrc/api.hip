@@ -198,10 +198,14 @@ fp8g_status_t fp8_gemm_nt_groupwise(const void* a, const void* b, const float* a
 namespace {
 
 // The contiguous form, with a's rows read directly (a_rows null, a_src_rows == m) or gathered.
+// With q_out non-null (the expert FFN's fc1), b holds gate then up rows (n = 2 inter) and the
+// epilogue writes silu(gate) * up, 1x128-quantised, to q_out / q_scale_out instead of out.
 void group_gemm_contiguous(const void* a, const float* a_scale, int64_t a_src_rows, const int32_t* a_rows,
                            const void* b, const float* b_scale, const int32_t* m_indices, void* out, int64_t m,
                            int64_t n, int64_t k, int64_t num_groups, int32_t scale_major, int32_t gran_m,
-                           int32_t gran_n, int32_t gran_k, void* stream, const char* what) {
+                           int32_t gran_n, int32_t gran_k, void* stream, const char* what,
+                           void* q_out = nullptr, float* q_scale_out = nullptr) {
+  const bool swiglu = q_out != nullptr;
   check_gemm_dims(m, n, k);
   check_gemm_dims(a_src_rows, n, k);
   require(num_groups >= 0 && num_groups <= kInt32Max, "num_groups must be in [0, 2^31)");
@@ -209,9 +213,14 @@ void group_gemm_contiguous(const void* a, const float* a_scale, int64_t a_src_ro
   check_scale_major(scale_major);
   check_granularity(gran_m, gran_n, gran_k);
   if (m == 0 || n == 0 || num_groups == 0) return;
-  check_operands(a, b, a_scale, b_scale, out, k);
+  check_operands(a, b, a_scale, b_scale, swiglu ? q_out : out, k);
   require(m_indices != nullptr && aligned(m_indices, 4), "m_indices must be non-null and 4-byte aligned");
   require(a_rows == nullptr || aligned(a_rows, 4), "a_rows must be 4-byte aligned");
+  if (swiglu) {
+    require(n % 256 == 0, "2*inter (%lld) must be a multiple of 256", (long long)n);
+    require(q_scale_out != nullptr && aligned(q_scale_out, 4) && aligned(q_out, 16),
+            "q_out must be 16-byte aligned and q_scale_out non-null and 4-byte aligned");
+  }
   require(k == 0 || a_src_rows > 0, "a must have at least one row");
   check_device();
   fp8g::GemmParams p{};
@@ -222,6 +231,9 @@ void group_gemm_contiguous(const void* a, const float* a_scale, int64_t a_src_ro
   p.out = static_cast<uint16_t*>(out);
   p.rowinfo = m_indices;
   p.a_rows = a_rows;
+  p.inter = (int32_t)(n / 2);
+  p.q_out = static_cast<uint8_t*>(q_out);
+  p.q_scale_out = q_scale_out;
   p.a_src_rows = (int32_t)a_src_rows;
   p.m = (int32_t)m;
   p.n = (int32_t)n;
@@ -238,15 +250,17 @@ void group_gemm_contiguous(const void* a, const float* a_scale, int64_t a_src_ro
   // counts two entries per 256-row tile.
   fp8g::TileConfig cfg = fp8g::TILE_128x256;
   if (fp8g::tile_override() >= 0) cfg = (fp8g::TileConfig)fp8g::tile_override();
+  if (swiglu && fp8g::tile_cols(cfg) != 256) cfg = fp8g::TILE_128x256;  // gate and up share a 256-wide tile
   p.tiles_m = (int32_t)(ceil_div(m, fp8g::tile_rows(cfg)) * (fp8g::tile_rows(cfg) / 128));
-  p.tiles_n = (int32_t)ceil_div(n, fp8g::tile_cols(cfg));
+  p.tiles_n = swiglu ? (int32_t)(n / 256) : (int32_t)ceil_div(n, fp8g::tile_cols(cfg));
   // 128-row tiles: the row tiles of one column tile run together and share b's slab in L2.
   // 256-row tiles: the column tiles of one row tile run together and share a's rows in L2 (each
   // expert's weights are streamed once either way); measured 1.8x faster for them.
   p.group_m = fp8g::tile_rows(cfg) == 256 ? 1 : p.tiles_m;
   const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
   require(grid <= kInt32Max, "too many tiles");
-  check_hip(fp8g::launch_gemm(fp8g::MODE_CONTIG, cfg, p, (int)grid, (hipStream_t)stream), what);
+  check_hip(fp8g::launch_gemm(swiglu ? fp8g::MODE_CONTIG_SWIGLU : fp8g::MODE_CONTIG, cfg, p, (int)grid,
+                              (hipStream_t)stream), what);
 }
 
 }  // namespace
@@ -274,6 +288,25 @@ fp8g_status_t fp8_group_gemm_contiguous_gather(const void* a, const float* a_sca
     require(m == 0 || a_rows != nullptr, "a_rows must be non-null");
     group_gemm_contiguous(a, a_scale, a_rows_total, a_rows, b, b_scale, m_indices, out, m, n, k, num_groups,
                           scale_major, gran_m, gran_n, gran_k, stream, "fp8_group_gemm_contiguous_gather launch");
+  });
+}
+
+fp8g_status_t fp8_moe_fc1_silu_quant(const void* a, const float* a_scale, int64_t a_rows_total,
+                                     const int32_t* a_rows, const void* w1, const float* w1_scale,
+                                     const int32_t* m_indices, void* q_out, float* q_scale_out, int64_t m,
+                                     int64_t inter, int64_t hidden, int64_t num_experts, int32_t scale_major,
+                                     int32_t gran_m, int32_t gran_n, int32_t gran_k, void* stream) {
+  return guarded([&] {
+    require(inter >= 0 && inter <= kInt32Max / 2, "inter must be in [0, 2^30)");
+    require(inter % 128 == 0, "inter (%lld) must be a multiple of 128", (long long)inter);
+    if (m == 0 || inter == 0 || num_experts == 0) {
+      check_gemm_dims(m, 2 * inter, hidden);
+      return;
+    }
+    require(q_out != nullptr, "q_out must be non-null");
+    group_gemm_contiguous(a, a_scale, a_rows == nullptr ? m : a_rows_total, a_rows, w1, w1_scale, m_indices, nullptr,
+                          m, 2 * inter, hidden, num_experts, scale_major, gran_m, gran_n, gran_k, stream,
+                          "fp8_moe_fc1_silu_quant launch", q_out, q_scale_out);
   });
 }
 

@@ -58,16 +58,89 @@ struct Tile {
   static_assert(STAGE_BYTES % 256 == 0, "stages keep the slabs' bank alignment");
   static_assert(BM % (SLAB_ROWS * NWAVES) == 0 && BN % (SLAB_ROWS * NWAVES) == 0, "slabs");
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "16x16 MFMA blocks");
-  static_assert(128 % WTN == 0, "a wave's columns must sit in one 128-wide b-scale block");
+  static_assert(128 % WTN == 0 || WTN == 128, "a wave's columns sit in one 128-wide b-scale block (two with SWIGLU)");
   static_assert(STAGES >= 2 && STAGES <= 4, "two to four LDS stages");
   static_assert((STAGES - 2) * LOADS < 64, "vmcnt range");
   static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
 };
 
+__device__ __forceinline__ float bf16_round(float x) { return (float)(__bf16)x; }  // RNE
+
+// Epilogue of the expert FFN's fc1 (CONTIG_SWIGLU): the values the unfused path would store in
+// BF16 -- gate and up of each output column -- are rounded to BF16 here too, then
+// h = silu(gate) * up with silu(g) = g / (1 + exp(-g)) in FP32, and each row's 128 h values of the
+// column tile are quantised to E4M3 with scale amax/448 (IEEE division; 1 for an all-zero block).
+// This is, operation for operation, what fp8_moe_silu_mul_quant does with the BF16 fc1 output, so
+// the codes and scales are identical. A row's 128 columns are spread over the WN waves of its row
+// block; their partial amax meet in LDS.
+template <typename T, int WN>
+__device__ __forceinline__ void swiglu_epilogue(const GemmParams& p, const f32x4 (&acc)[T::IG][T::JG], uint8_t* smem,
+                                                int row0, int row_end, int bsel, int tn, int i0, int wave, int lane,
+                                                bool wave_live) {
+  constexpr int OUTW = 128 / WN;
+  constexpr int HALF = T::JG / 2;  // column groups of gate (then the same number of up)
+  const int fr = lane & 15, q = wave % WN;
+  float h[T::IG][HALF][4];
+  float part[T::IG];
+#pragma unroll
+  for (int ig = 0; ig < T::IG; ++ig) {
+    float m = 0.0f;
+#pragma unroll
+    for (int jg = 0; jg < HALF; ++jg)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float g = bf16_round(acc[ig][jg][r]), u = bf16_round(acc[ig][HALF + jg][r]);
+        h[ig][jg][r] = __fdiv_rn(g, 1.0f + expf(-g)) * u;
+        m = fmaxf(m, fabsf(h[ig][jg][r]));
+      }
+    m = fmaxf(m, __shfl_xor(m, 16, 64));  // the four lane groups hold the wave's columns of a row
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    part[ig] = m;
+  }
+  // partial amax per (wave column q, tile row): the main loop's stages are free after this barrier
+  float* amax_lds = reinterpret_cast<float*>(smem);
+  lds_pipeline_barrier();
+  if (lane < 16) {
+#pragma unroll
+    for (int ig = 0; ig < T::IG; ++ig) amax_lds[q * 256 + i0 + ig * 16 + fr] = part[ig];
+  }
+  lds_pipeline_barrier();
+  if (!wave_live) return;
+  const int nblk = p.inter / 128;
+  const int cl = (lane >> 4) * 4;
+#pragma unroll
+  for (int ig = 0; ig < T::IG; ++ig) {
+    const int tr = i0 + ig * 16 + fr;  // tile row
+    const int i = row0 + tr;
+    if (i >= row_end || p.rowinfo[i] != bsel) continue;
+    float amax = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WN; ++w) amax = fmaxf(amax, amax_lds[w * 256 + tr]);
+    const float sc = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+    uint8_t* orow = p.q_out + (int64_t)i * p.inter + 128 * tn + q * OUTW;
+#pragma unroll
+    for (int jg = 0; jg < HALF; ++jg) {
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = __fdiv_rn(h[ig][jg][r], sc);
+      int w4 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+      w4 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w4, true);
+      *reinterpret_cast<int*>(orow + jg * 16 + cl) = w4;
+    }
+    if (q == 0 && lane < 16) p.q_scale_out[(int64_t)i * nblk + tn] = sc;
+  }
+}
+
 template <int BM, int BN, int WM, int WN, int STAGES, int MODE>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_fp8_groupwise_kernel(const GemmParams p) {
   using T = Tile<BM, BN, WM, WN, STAGES>;
+  constexpr bool CONTIG = MODE == MODE_CONTIG || MODE == MODE_CONTIG_SWIGLU;
+  constexpr bool SWIGLU = MODE == MODE_CONTIG_SWIGLU;
+  // SWIGLU: wave column q of the WN holds the gate and the up columns of OUTW output columns; its
+  // b rows ("virtual columns" v of the tile) are OUTW gate rows then OUTW up rows.
+  constexpr int OUTW = SWIGLU ? 128 / WN : 0;
+  static_assert(!SWIGLU || (BN == 256 && T::WTN == 2 * (128 / WN)), "SWIGLU tiles are 256 wide");
   // first of the loads issued during column group jg (the LOADS loads spread over JG groups)
   constexpr int LG = T::JG < LOAD_GROUPS ? T::JG : LOAD_GROUPS;
   constexpr auto load_first = [](int jg) { return ((jg < LG ? jg : LG) * T::LOADS + LG - 1) / LG; };
@@ -89,7 +162,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   // Contiguous form with 256-row tiles: the grid holds two entries per row tile (tm = 2 * tile +
   // half), so a tile whose two 128-row halves belong to different experts runs as two workgroups.
   int half = 0;
-  if (MODE == MODE_CONTIG && BM == 256) {
+  if (CONTIG && BM == 256) {
     half = tm & 1;
     tm >>= 1;
   }
@@ -109,7 +182,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     if (row0 >= mm) return;
     row_end = mm;
     bsel = g;
-  } else if (MODE == MODE_CONTIG) {
+  } else if (CONTIG) {
     constexpr int HALVES = BM / 128;
     int ex[HALVES];
 #pragma unroll
@@ -140,10 +213,15 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   // clamped to the last valid row), so the pipeline can wait on a fixed count of outstanding loads.
   const int lrow = lane >> 3;
   const int a_last = row_end - 1;
+  // SWIGLU: b row of virtual column v of column tile tn (output columns [128 tn, 128 tn + 128))
+  auto swiglu_b_row = [&](int v) {
+    const int q = v / (2 * OUTW), r = v % (2 * OUTW);
+    return (r < OUTW ? 0 : p.inter) + 128 * tn + q * OUTW + (r % OUTW);
+  };
   // The row of a (and of a_scale) that tile row r reads: r itself, or a_rows[r] when the contiguous
   // form gathers its rows (rows whose index is out of range read row 0; they are never stored).
   auto a_source_row = [&](int r) {
-    if (MODE != MODE_CONTIG || p.a_rows == nullptr) return r;
+    if (!CONTIG || p.a_rows == nullptr) return r;
     const int s = p.a_rows[r];
     return (s >= 0 && s < p.a_src_rows) ? s : 0;
   };
@@ -159,7 +237,8 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   for (int q = 0; q < T::B_LOADS; ++q) {
     const int slab_row = (wave * T::B_LOADS + q) * SLAB_ROWS;
     const int lchunk = (lane & 7) ^ swizzle(slab_row + lrow);
-    const int r = min(col0 + slab_row + lrow, p.n - 1);
+    int r = min(col0 + slab_row + lrow, p.n - 1);
+    if (SWIGLU) r = swiglu_b_row(slab_row + lrow);
     b_off[q] = (uint32_t)r * (uint32_t)p.k + lchunk * 16;
   }
 
@@ -179,7 +258,8 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     s_voff = (uint32_t)r * p.sa_row_stride * 4;
     s_dst = T::SA_OFF + wave * 256;
   } else {
-    const int nb = min(col0 / 128 + lane, p.nblocks - 1);
+    const int nb = SWIGLU ? min((lane == 0 ? 0 : p.inter / 128) + tn, p.nblocks - 1)
+                          : min(col0 / 128 + lane, p.nblocks - 1);
     s_voff = (uint32_t)nb * p.sb_nb_stride * 4;
     s_dst = T::SB_OFF;
   }
@@ -197,7 +277,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   bool wave_live = (row0 + i0 < row_end) && (col0 + j0 < p.n) && ((half_mask >> (i0 / 128)) & 1);
   // In the contiguous form a wave none of whose rows belongs to the expert holds padding (or the
   // other half's rows) only: one m_indices entry per lane, WTM == 64.
-  if (MODE == MODE_CONTIG) {
+  if (CONTIG) {
     static_assert(T::WTM == 64, "one lane per wave row");
     wave_live = wave_live && __ballot(p.rowinfo[row0 + i0 + lane] == bsel) != 0;
   }
@@ -240,10 +320,16 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     const uint8_t* sA = smem + (kb % STAGES) * T::STAGE_BYTES;
     const uint8_t* sB = sA + T::A_BYTES;
     const float* sSA = reinterpret_cast<const float*>(sA + T::SA_OFF);
-    const float sbv = reinterpret_cast<const float*>(sA + T::SB_OFF)[(col0 + j0) / 128 - col0 / 128];
-    float s[T::IG];
+    const float* sSB = reinterpret_cast<const float*>(sA + T::SB_OFF);
+    const float sbv = SWIGLU ? sSB[0] : sSB[(col0 + j0) / 128 - col0 / 128];
+    const float sbv_up = SWIGLU ? sSB[1] : sbv;  // SWIGLU: the up columns' block
+    float s[T::IG], s_up[T::IG];
 #pragma unroll
-    for (int ig = 0; ig < T::IG; ++ig) s[ig] = sSA[i0 + ig * 16 + fr] * sbv;
+    for (int ig = 0; ig < T::IG; ++ig) {
+      const float sav = sSA[i0 + ig * 16 + fr];
+      s[ig] = sav * sbv;
+      s_up[ig] = SWIGLU ? sav * sbv_up : s[ig];
+    }
     i32x8 af[T::IG];
 #pragma unroll
     for (int ig = 0; ig < T::IG; ++ig) af[ig] = load_frag(sA, i0 + ig * 16 + fr, lane);
@@ -264,7 +350,8 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
             bq[jg], af[ig], f32x4{0.f, 0.f, 0.f, 0.f}, FMT_E4M3, FMT_E4M3, 0, E8M0_ONE, 0, E8M0_ONE);
         if (jg > 0) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[ig][jg - 1][r] = __builtin_fmaf(prod[jg - 1][ig][r], s[ig], acc[ig][jg - 1][r]);
+          for (int r = 0; r < 4; ++r)
+            acc[ig][jg - 1][r] = __builtin_fmaf(prod[jg - 1][ig][r], jg - 1 < T::JG / 2 ? s[ig] : s_up[ig], acc[ig][jg - 1][r]);
         }
       }
       sched_vmem_group(load_first(jg + 1) - load_first(jg));
@@ -280,7 +367,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
 #pragma unroll
     for (int ig = 0; ig < T::IG; ++ig)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[ig][T::JG - 1][r] = __builtin_fmaf(prod[T::JG - 1][ig][r], s[ig], acc[ig][T::JG - 1][r]);
+      for (int r = 0; r < 4; ++r) acc[ig][T::JG - 1][r] = __builtin_fmaf(prod[T::JG - 1][ig][r], s_up[ig], acc[ig][T::JG - 1][r]);
   };
 
   // Pipeline: K block kb (slabs and scales) lives in stage kb % STAGES. Iteration kb waits until
@@ -310,6 +397,11 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   }
   wait_vmcnt<0>();  // the zero-fill loads of the last iterations
 
+  if constexpr (SWIGLU) {
+    swiglu_epilogue<T, WN>(p, acc, smem, row0, row_end, bsel, tn, i0, wave, lane, wave_live);
+    return;
+  }
+
   // ---- epilogue: BF16 round-to-nearest-even, 8-byte stores of valid rows ---------------------
   if (wave_live) {
   uint16_t* O = p.out + (int64_t)g * p.out_group_stride;
@@ -318,7 +410,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   for (int ig = 0; ig < T::IG; ++ig) {
     const int i = row0 + i0 + ig * 16 + fr;
     bool ok = i < row_end;
-    if (MODE == MODE_CONTIG) ok = ok && p.rowinfo[i] == bsel;
+    if (CONTIG) ok = ok && p.rowinfo[i] == bsel;
     if (!ok) continue;
     uint16_t* orow = O + (int64_t)i * p.n;
 #pragma unroll
@@ -349,6 +441,13 @@ hipError_t launch_cfg(GemmMode mode, const GemmParams& p, int grid, hipStream_t 
     case MODE_MASKED:
       hipLaunchKernelGGL((gemm_fp8_groupwise_kernel<BM, BN, WM, WN, STAGES, MODE_MASKED>), dim3(grid), block, 0, stream, p);
       break;
+    case MODE_CONTIG_SWIGLU:
+      if constexpr (BN == 256) {
+        hipLaunchKernelGGL((gemm_fp8_groupwise_kernel<BM, BN, WM, WN, STAGES, MODE_CONTIG_SWIGLU>), dim3(grid), block, 0,
+                           stream, p);
+        break;
+      }
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -11,6 +11,7 @@ enum GemmMode : int {
   MODE_PLAIN = 0,   // out = a @ b.T
   MODE_CONTIG = 1,  // per 128-row tile, b chosen by the tile's expert in m_indices
   MODE_MASKED = 2,  // per group g, rows below masked_m[g]
+  MODE_CONTIG_SWIGLU = 3,  // contiguous, epilogue silu(gate) * up -> 1x128 E4M3 (expert-FFN fc1)
 };
 
 // Everything the GEMM kernel needs, passed by value as the kernel argument. Strides in elements.
@@ -23,6 +24,12 @@ struct GemmParams {
   const int32_t* rowinfo;  // m_indices (CONTIG) or masked_m (MASKED)
   const int32_t* a_rows;   // CONTIG only: row r of the product takes row a_rows[r] of a; null: r
   int32_t a_src_rows;      // rows of a (and of a_scale) in memory
+  // CONTIG_SWIGLU: b holds gate rows [0, inter) then up rows [inter, 2 inter); column tile t
+  // computes gate and up of output columns [128 t, 128 t + 128) and writes
+  // q_out[r][c] = E4M3(silu(gate) * up / q_scale_out[r][t]) with a 1x128 scale per row and tile.
+  int32_t inter;
+  uint8_t* q_out;
+  float* q_scale_out;
   int64_t a_group_stride, b_group_stride, sa_group_stride, sb_group_stride, out_group_stride;
   int32_t m;  // PLAIN/CONTIG: rows of a; MASKED: max_m
   int32_t n, k;

@@ -5,9 +5,10 @@ MoE FP8 (cudarc)"): BF16 tokens, int32 top-k expert ids, FP8 fc1 weights (E, 2*i
 first ``inter`` rows are the gate and the next ``inter`` the up projection, FP8 fc2 weights
 (E, hidden, inter), 128x128 FP32 block scales, and the top-k routing weights for the combine.
 
-Six library calls on the current stream, no host synchronisation:
+Five library calls on the current stream, no host synchronisation:
   permutation -> quantise the tokens -> fc1 grouped GEMM reading the token rows through the
-  permutation -> SiLU-mul+quantise -> fc2 grouped GEMM -> combine
+  permutation, with SiLU-mul+quantise in its epilogue -> fc2 grouped GEMM -> combine
+(``fuse_activation=False`` runs fc1 and the activation as two calls, with the same result).
 """
 
 from __future__ import annotations
@@ -17,7 +18,8 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from .gemm import _check, _require_cuda, _stream, fp8_group_gemm_contiguous, fp8_group_gemm_contiguous_gather
+from .gemm import (_FP8_DTYPES, _GRAN, _check, _major, _ptr, _require_cuda, _stream, fp8_group_gemm_contiguous,
+                   fp8_group_gemm_contiguous_gather)
 
 
 def default_m_alloc(num_tokens: int, top_k: int, num_experts: int) -> int:
@@ -108,6 +110,35 @@ def moe_silu_mul_quant(y, m_indices, a_out, a_scale_out):
     _lib.check(st, "fp8_moe_silu_mul_quant")
 
 
+def moe_fc1_silu_quant(a, a_scale, a_rows, w1, w1_scale, m_indices, q_out, q_scale_out, scale_major="K"):
+    """fc1 and SiLU(gate)*up -> 1x128 E4M3 in one pass (rows of a read through a_rows, or a itself if None)."""
+    dev = _require_cuda(a)
+    rows_total, hidden = a.shape
+    m = m_indices.shape[0]
+    num_experts, two_inter, _ = w1.shape
+    inter = two_inter // 2
+    kb, nb = hidden // 128, two_inter // 128
+    major = _major(scale_major)
+    _check(a, "a", _FP8_DTYPES, (rows_total, hidden), dev)
+    _check(a_scale, "a_scale", (torch.float32,), (rows_total, kb) if major == 0 else (kb, rows_total), dev)
+    if a_rows is None:
+        if rows_total != m:
+            raise ValueError(f"without a_rows, a must have m = {m} rows")
+    else:
+        _check(a_rows, "a_rows", (torch.int32,), (m,), dev)
+    _check(w1, "w1", _FP8_DTYPES, (num_experts, two_inter, hidden), dev)
+    _check(w1_scale, "w1_scale", (torch.float32,), (num_experts, nb, kb) if major == 0 else (num_experts, kb, nb), dev)
+    _check(m_indices, "m_indices", (torch.int32,), (m,), dev)
+    _check(q_out, "q_out", (torch.uint8, torch.float8_e4m3fn), (m, inter), dev)
+    _check(q_scale_out, "q_scale_out", (torch.float32,), (m, inter // 128), dev)
+    with torch.cuda.device(dev):
+        st = _lib.load().fp8_moe_fc1_silu_quant(_ptr(a), _ptr(a_scale), rows_total,
+                                                None if a_rows is None else _ptr(a_rows), _ptr(w1), _ptr(w1_scale),
+                                                _ptr(m_indices), _ptr(q_out), _ptr(q_scale_out), m, inter, hidden,
+                                                num_experts, major, *_GRAN, _stream(dev))
+    _lib.check(st, "fp8_moe_fc1_silu_quant")
+
+
 def moe_combine(y, row_of_entry, topk_weights, out):
     dev = _require_cuda(y)
     m_alloc, h = y.shape
@@ -122,8 +153,12 @@ def moe_combine(y, row_of_entry, topk_weights, out):
     _lib.check(st, "fp8_moe_combine")
 
 
-def moe_ffn_fp8_block_scale(x, topk_ids, topk_weights, w1, s1, w2, s2, out=None, workspace=None):
-    """Expert FFN: out (T, hidden) bf16. ``workspace`` (MoeWorkspace) keeps every intermediate."""
+def moe_ffn_fp8_block_scale(x, topk_ids, topk_weights, w1, s1, w2, s2, out=None, workspace=None,
+                            fuse_activation=True):
+    """Expert FFN: out (T, hidden) bf16. ``workspace`` (MoeWorkspace) keeps every intermediate.
+
+    ``fuse_activation`` runs fc1 and SiLU-mul+requant as one pass (workspace.y1 is then not written);
+    the result is bit-identical either way."""
     num_tokens, hidden = x.shape
     num_experts, two_inter, _ = w1.shape
     inter = two_inter // 2
@@ -135,8 +170,11 @@ def moe_ffn_fp8_block_scale(x, topk_ids, topk_weights, w1, s1, w2, s2, out=None,
         out = torch.empty((num_tokens, hidden), dtype=torch.bfloat16, device=x.device)
     moe_build_permutation(topk_ids, num_experts, ws.m_indices, ws.src_token, ws.row_of_entry)
     moe_gather_quant(x, None, ws.a1, ws.sa1)
-    fp8_group_gemm_contiguous_gather(ws.a1, ws.sa1, ws.src_token, w1, s1, ws.m_indices, ws.y1)
-    moe_silu_mul_quant(ws.y1, ws.m_indices, ws.a2, ws.sa2)
+    if fuse_activation:
+        moe_fc1_silu_quant(ws.a1, ws.sa1, ws.src_token, w1, s1, ws.m_indices, ws.a2, ws.sa2)
+    else:
+        fp8_group_gemm_contiguous_gather(ws.a1, ws.sa1, ws.src_token, w1, s1, ws.m_indices, ws.y1)
+        moe_silu_mul_quant(ws.y1, ws.m_indices, ws.a2, ws.sa2)
     fp8_group_gemm_contiguous(ws.a2, w2, ws.sa2, s2, ws.m_indices, ws.y2)
     moe_combine(ws.y2, ws.row_of_entry, topk_weights, out)
     return out

@@ -8,6 +8,8 @@ every other code and every scale must match. The GEMMs and the combine are held 
 tolerance on the oracle fed the GPU's own inputs.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -21,11 +23,23 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _run(d):
+def _ffn(d, fuse):
     ws = fp8g.MoeWorkspace.allocate(d["num_tokens"], d["top_k"], d["num_experts"], d["hidden"], d["inter"], DEV)
     out = fp8g.moe_ffn_fp8_block_scale(d["x"], d["topk_ids"], d["topk_weights"], d["w1"], d["s1"], d["w2"],
-                                       d["s2"], workspace=ws)
+                                       d["s2"], workspace=ws, fuse_activation=fuse)
     torch.cuda.synchronize()
+    return out, ws
+
+
+def _run(d):
+    """The unfused chain (every intermediate kept for the stage checks), and the fused fc1 +
+    activation, which must produce the same bytes."""
+    out, ws = _ffn(d, fuse=False)
+    out_f, ws_f = _ffn(d, fuse=True)
+    valid = host(ws.m_indices) >= 0
+    assert np.array_equal(host(ws_f.a2)[valid], host(ws.a2)[valid]), "fused fc1 activation codes differ"
+    assert np.array_equal(host(ws_f.sa2)[valid], host(ws.sa2)[valid]), "fused fc1 activation scales differ"
+    assert np.array_equal(host(out_f), host(out))
     return out, ws
 
 
@@ -110,6 +124,41 @@ def test_permutation_matches_oracle(num_tokens, top_k, num_experts):
     assert np.array_equal(host(m_indices), p["m_indices"])
     assert np.array_equal(host(src_token), p["src_token"])
     assert np.array_equal(host(row_of_entry).reshape(-1), p["row_of_entry"].reshape(-1))
+
+
+@pytest.mark.parametrize("tile,gathered", [("128x256", True), ("256x256", True), ("128x256", False)])
+def test_fc1_silu_quant_equals_gemm_then_activation(tile, gathered):
+    """fp8_moe_fc1_silu_quant against fc1 (BF16 out) followed by the activation kernel, byte for byte."""
+    say("fused fc1 + activation", tile, "gathered" if gathered else "direct")
+    d = workloads.moe(num_tokens=300, hidden=512, num_experts=5, top_k=3, inter=384, seed=9, device=DEV)
+    ws = fp8g.MoeWorkspace.allocate(300, 3, 5, 512, 384, DEV)
+    fp8g.moe_build_permutation(d["topk_ids"], 5, ws.m_indices, ws.src_token, ws.row_of_entry)
+    fp8g.moe_gather_quant(d["x"], None, ws.a1, ws.sa1)
+    if gathered:
+        a, sa, rows = ws.a1, ws.sa1, ws.src_token
+    else:
+        g = ws.src_token.clamp(min=0).long()
+        a, sa, rows = ws.a1[g].contiguous(), ws.sa1[g].contiguous(), None
+    y = torch.empty((ws.m_alloc, 768), dtype=torch.bfloat16, device=DEV)
+    q_ref = torch.full((ws.m_alloc, 384), 0x11, dtype=torch.uint8, device=DEV)
+    s_ref = torch.full((ws.m_alloc, 3), -1.0, device=DEV)
+    q = q_ref.clone()
+    s = s_ref.clone()
+    try:
+        os.environ["FP8G_TILE"] = tile
+        if gathered:
+            fp8g.fp8_group_gemm_contiguous_gather(a, sa, rows, d["w1"], d["s1"], ws.m_indices, y)
+        else:
+            fp8g.fp8_group_gemm_contiguous(a, d["w1"], sa, d["s1"], ws.m_indices, y)
+        fp8g.moe_silu_mul_quant(y, ws.m_indices, q_ref, s_ref)
+        fp8g.moe_fc1_silu_quant(a, sa, rows, d["w1"], d["s1"], ws.m_indices, q, s)
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("FP8G_TILE", None)
+    valid = host(ws.m_indices) >= 0
+    assert np.array_equal(host(q)[valid], host(q_ref)[valid])
+    assert np.array_equal(host(s)[valid], host(s_ref)[valid])
+    assert (host(q)[~valid] == 0x11).all() and (host(s)[~valid] == -1.0).all()
 
 
 def test_moe_small_all_stages_and_end_to_end():
