@@ -16,7 +16,8 @@
  *     fp8g_last_error() returns (thread-local, valid until the thread's next fp8g call).
  *   - An unsupported device (anything but gfx950) is an error (FP8G_NOT_SUPPORTED), never a fallback.
  *   - Tensors are dense and row-major ("contiguous"); E4M3 means OCP E4M3FN (bias 7, max 448,
- *     NaN = S.1111.111, no infinities), one byte per element. BF16 outputs are round-to-nearest-even.
+ *     NaN = S.1111.111, no infinities), one byte per element. BF16 and FP16 outputs are
+ *     round-to-nearest-even.
  *   - Pointers must be 16-byte aligned (E4M3 operands, outputs) or 4-byte aligned (scales, indices).
  *   - Output rows that the operation leaves unspecified are not written.
  *
@@ -25,10 +26,11 @@
  * FP8G_NOT_SUPPORTED. k must be a multiple of 128 and n a multiple of 128.
  *
  * Arithmetic (MATE FlashInfer-API page, section "GEMM"): for every output element
- *     out[i][j] = bf16( sum_kb  sa(i,kb) * sb(j/128,kb) * sum_{k in block kb} a[i][k] * b[j][k] )
+ *     out[i][j] = cvt( sum_kb  sa(i,kb) * sb(j/128,kb) * sum_{k in block kb} a[i][k] * b[j][k] )
  * where each 128-wide block sum is one FP8 matrix-core product accumulated in FP32 and the scale
- * product is applied by one FP32 multiply-add per K block. Results do not depend on `expected_m`
- * or on the tile configuration the library picks.
+ * product is applied by one FP32 multiply-add per K block; cvt rounds the FP32 sum to the output
+ * type (out_dtype: BF16 by default, or FP16 -- the page's out_dtype). Results do not depend on
+ * `expected_m` or on the tile configuration the library picks.
  */
 #ifndef FP8G_H_
 #define FP8G_H_
@@ -54,6 +56,11 @@ typedef enum {
 } fp8g_status_t;
 
 typedef enum {
+  FP8G_OUT_BF16 = 0, /* bfloat16 */
+  FP8G_OUT_FP16 = 1  /* IEEE binary16; values beyond its range become +-inf */
+} fp8g_out_dtype_t;
+
+typedef enum {
   FP8G_SCALE_K_MAJOR = 0,  /* a_scale (m, k/128), b_scale (n/128, k/128) */
   FP8G_SCALE_MN_MAJOR = 1  /* a_scale (k/128, m), b_scale (k/128, n/128) */
 } fp8g_scale_major_t;
@@ -71,13 +78,13 @@ FP8G_API int32_t fp8g_version(void);
  *   b        (n, k)  E4M3, row-major (the product is a @ b.T)
  *   a_scale  FP32, (m, k/128) when scale_major = K-major, (k/128, m) when MN-major
  *   b_scale  FP32, (n/128, k/128) when K-major, (k/128, n/128) when MN-major
- *   out      (m, n)  BF16, fully written
+ *   out      (m, n)  BF16 or FP16 (out_dtype), fully written
  * m >= 0 is arbitrary; n and k are multiples of 128. m == 0 or n == 0 is a no-op; k == 0 writes
  * zeros. scale_major applies to both scale tensors.
  */
 FP8G_API fp8g_status_t fp8_gemm_nt_groupwise(const void* a, const void* b, const float* a_scale,
-                                    const float* b_scale, void* out, int64_t m, int64_t n,
-                                    int64_t k, int32_t scale_major, int32_t gran_m,
+                                    const float* b_scale, void* out, int32_t out_dtype, int64_t m,
+                                    int64_t n, int64_t k, int32_t scale_major, int32_t gran_m,
                                     int32_t gran_n, int32_t gran_k, void* stream);
 
 /*
@@ -90,14 +97,15 @@ FP8G_API fp8g_status_t fp8_gemm_nt_groupwise(const void* a, const void* b, const
  *   m_indices  (m,) int32 expert of every row; -1 marks a padding row. Each expert's rows occupy a
  *              contiguous, 128-row-aligned region, so every aligned 128-row tile holds one expert
  *              and padding. The tile's expert is the largest index among its rows.
- *   out        (m, n) BF16; rows whose m_indices is -1 (or is not the tile's expert) are not
- *              written.
+ *   out        (m, n) BF16 or FP16 (out_dtype); rows whose m_indices is -1 (or is not the tile's
+ *              expert) are not written.
  * Indices outside [-1, num_groups) are treated as padding. The MN-major layout is an extension
  * (the page defines the grouped forms with K-major scales only).
  */
 FP8G_API fp8g_status_t fp8_group_gemm_contiguous(const void* a, const void* b, const float* a_scale,
                                         const float* b_scale, const int32_t* m_indices, void* out,
-                                        int64_t m, int64_t n, int64_t k, int64_t num_groups,
+                                        int32_t out_dtype, int64_t m, int64_t n, int64_t k,
+                                        int64_t num_groups,
                                         int32_t scale_major, int32_t gran_m, int32_t gran_n,
                                         int32_t gran_k, void* stream);
 
@@ -117,8 +125,8 @@ FP8G_API fp8g_status_t fp8_group_gemm_contiguous(const void* a, const void* b, c
 FP8G_API fp8g_status_t fp8_group_gemm_contiguous_gather(const void* a, const float* a_scale,
                                                int64_t a_rows_total, const int32_t* a_rows,
                                                const void* b, const float* b_scale,
-                                               const int32_t* m_indices, void* out, int64_t m,
-                                               int64_t n, int64_t k, int64_t num_groups,
+                                               const int32_t* m_indices, void* out, int32_t out_dtype,
+                                               int64_t m, int64_t n, int64_t k, int64_t num_groups,
                                                int32_t scale_major, int32_t gran_m, int32_t gran_n,
                                                int32_t gran_k, void* stream);
 
@@ -132,11 +140,13 @@ FP8G_API fp8g_status_t fp8_group_gemm_contiguous_gather(const void* a, const flo
  *   masked_m   (num_groups,) int32 valid rows per group, read on the device; values are clamped
  *              into [0, max_m]
  *   expected_m host-side hint of the typical masked_m, used only to pick a tile configuration
- *   out        (num_groups, max_m, n) BF16; rows at or beyond masked_m[g] are not written
+ *   out        (num_groups, max_m, n) BF16 or FP16 (out_dtype); rows at or beyond masked_m[g] are
+ *              not written
  */
 FP8G_API fp8g_status_t fp8_batch_gemm_masked(const void* a, const void* b, const float* a_scale,
                                     const float* b_scale, const int32_t* masked_m,
-                                    int64_t expected_m, void* out, int64_t num_groups,
+                                    int64_t expected_m, void* out, int32_t out_dtype,
+                                    int64_t num_groups,
                                     int64_t max_m, int64_t n, int64_t k, int32_t scale_major,
                                     int32_t gran_m, int32_t gran_n, int32_t gran_k, void* stream);
 

@@ -13,6 +13,7 @@ _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG_DIR, "libfp8g.so")
 
 OK, INVALID_ARGUMENT, NOT_SUPPORTED, HIP_ERROR, INTERNAL = 0, 1, 2, 3, 4
+OUT_BF16, OUT_FP16 = 0, 1
 SCALE_K_MAJOR, SCALE_MN_MAJOR = 0, 1
 
 _P = ctypes.c_void_p
@@ -23,13 +24,13 @@ _I32 = ctypes.c_int32
 SIGNATURES = {
     "fp8g_last_error": ([], ctypes.c_char_p),
     "fp8g_version": ([], _I32),
-    "fp8_gemm_nt_groupwise": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P], _I32),
-    "fp8_group_gemm_contiguous": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P],
+    "fp8_gemm_nt_groupwise": ([_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P], _I32),
+    "fp8_group_gemm_contiguous": ([_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P],
                                   _I32),
-    "fp8_group_gemm_contiguous_gather": ([_P, _P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32,
-                                          _I32, _P], _I32),
-    "fp8_batch_gemm_masked": ([_P, _P, _P, _P, _P, _I64, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P],
-                              _I32),
+    "fp8_group_gemm_contiguous_gather": ([_P, _P, _I64, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _I32, _I32,
+                                          _I32, _I32, _P], _I32),
+    "fp8_batch_gemm_masked": ([_P, _P, _P, _P, _P, _I64, _P, _I32, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32,
+                               _P], _I32),
     "fp8_moe_build_permutation": ([_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P], _I32),
     "fp8_moe_gather_quant": ([_P, _P, _I64, _I64, _I64, _P, _P, _P], _I32),
     "fp8_moe_silu_mul_quant": ([_P, _P, _I64, _I64, _P, _P, _P], _I32),

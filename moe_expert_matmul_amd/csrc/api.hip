@@ -79,6 +79,10 @@ void check_granularity(int32_t gm, int32_t gn, int32_t gk) {
     fail(FP8G_NOT_SUPPORTED, "scale granularity (%d,%d,%d) not supported; only (1,128,128)", gm, gn, gk);
 }
 
+void check_out_dtype(int32_t dt) {
+  require(dt == FP8G_OUT_BF16 || dt == FP8G_OUT_FP16, "out_dtype must be 0 (BF16) or 1 (FP16), got %d", dt);
+}
+
 void check_scale_major(int32_t sm) {
   require(sm == FP8G_SCALE_K_MAJOR || sm == FP8G_SCALE_MN_MAJOR, "scale_major must be 0 (K) or 1 (MN), got %d", sm);
 }
@@ -158,13 +162,14 @@ const char* fp8g_last_error(void) { return g_last_error.c_str(); }
 int32_t fp8g_version(void) { return 100; }  // 0.1.0
 
 fp8g_status_t fp8_gemm_nt_groupwise(const void* a, const void* b, const float* a_scale,
-                                    const float* b_scale, void* out, int64_t m, int64_t n,
-                                    int64_t k, int32_t scale_major, int32_t gran_m,
+                                    const float* b_scale, void* out, int32_t out_dtype, int64_t m,
+                                    int64_t n, int64_t k, int32_t scale_major, int32_t gran_m,
                                     int32_t gran_n, int32_t gran_k, void* stream) {
   return guarded([&] {
     check_gemm_dims(m, n, k);
     check_scale_major(scale_major);
     check_granularity(gran_m, gran_n, gran_k);
+    check_out_dtype(out_dtype);
     if (m == 0 || n == 0) return;
     check_operands(a, b, a_scale, b_scale, out, k);
     check_device();
@@ -174,6 +179,7 @@ fp8g_status_t fp8_gemm_nt_groupwise(const void* a, const void* b, const float* a
     p.sa = a_scale;
     p.sb = b_scale;
     p.out = static_cast<uint16_t*>(out);
+    p.out_fp16 = out_dtype == FP8G_OUT_FP16;
     p.m = (int32_t)m;
     p.n = (int32_t)n;
     p.k = (int32_t)k;
@@ -204,8 +210,9 @@ void group_gemm_contiguous(const void* a, const float* a_scale, int64_t a_src_ro
                            const void* b, const float* b_scale, const int32_t* m_indices, void* out, int64_t m,
                            int64_t n, int64_t k, int64_t num_groups, int32_t scale_major, int32_t gran_m,
                            int32_t gran_n, int32_t gran_k, void* stream, const char* what,
-                           void* q_out = nullptr, float* q_scale_out = nullptr) {
+                           int32_t out_dtype = FP8G_OUT_BF16, void* q_out = nullptr, float* q_scale_out = nullptr) {
   const bool swiglu = q_out != nullptr;
+  check_out_dtype(out_dtype);
   check_gemm_dims(m, n, k);
   check_gemm_dims(a_src_rows, n, k);
   require(num_groups >= 0 && num_groups <= kInt32Max, "num_groups must be in [0, 2^31)");
@@ -229,6 +236,7 @@ void group_gemm_contiguous(const void* a, const float* a_scale, int64_t a_src_ro
   p.sa = a_scale;
   p.sb = b_scale;
   p.out = static_cast<uint16_t*>(out);
+  p.out_fp16 = out_dtype == FP8G_OUT_FP16;
   p.rowinfo = m_indices;
   p.a_rows = a_rows;
   p.inter = (int32_t)(n / 2);
@@ -269,25 +277,26 @@ extern "C" {
 
 fp8g_status_t fp8_group_gemm_contiguous(const void* a, const void* b, const float* a_scale,
                                         const float* b_scale, const int32_t* m_indices, void* out,
-                                        int64_t m, int64_t n, int64_t k, int64_t num_groups,
-                                        int32_t scale_major, int32_t gran_m, int32_t gran_n,
-                                        int32_t gran_k, void* stream) {
+                                        int32_t out_dtype, int64_t m, int64_t n, int64_t k,
+                                        int64_t num_groups, int32_t scale_major, int32_t gran_m,
+                                        int32_t gran_n, int32_t gran_k, void* stream) {
   return guarded([&] {
     group_gemm_contiguous(a, a_scale, m, nullptr, b, b_scale, m_indices, out, m, n, k, num_groups, scale_major,
-                          gran_m, gran_n, gran_k, stream, "fp8_group_gemm_contiguous launch");
+                          gran_m, gran_n, gran_k, stream, "fp8_group_gemm_contiguous launch", out_dtype);
   });
 }
 
 fp8g_status_t fp8_group_gemm_contiguous_gather(const void* a, const float* a_scale, int64_t a_rows_total,
                                                const int32_t* a_rows, const void* b, const float* b_scale,
-                                               const int32_t* m_indices, void* out, int64_t m, int64_t n,
-                                               int64_t k, int64_t num_groups, int32_t scale_major,
-                                               int32_t gran_m, int32_t gran_n, int32_t gran_k,
-                                               void* stream) {
+                                               const int32_t* m_indices, void* out, int32_t out_dtype,
+                                               int64_t m, int64_t n, int64_t k, int64_t num_groups,
+                                               int32_t scale_major, int32_t gran_m, int32_t gran_n,
+                                               int32_t gran_k, void* stream) {
   return guarded([&] {
     require(m == 0 || a_rows != nullptr, "a_rows must be non-null");
     group_gemm_contiguous(a, a_scale, a_rows_total, a_rows, b, b_scale, m_indices, out, m, n, k, num_groups,
-                          scale_major, gran_m, gran_n, gran_k, stream, "fp8_group_gemm_contiguous_gather launch");
+                          scale_major, gran_m, gran_n, gran_k, stream, "fp8_group_gemm_contiguous_gather launch",
+                          out_dtype);
   });
 }
 
@@ -306,21 +315,23 @@ fp8g_status_t fp8_moe_fc1_silu_quant(const void* a, const float* a_scale, int64_
     require(q_out != nullptr, "q_out must be non-null");
     group_gemm_contiguous(a, a_scale, a_rows == nullptr ? m : a_rows_total, a_rows, w1, w1_scale, m_indices, nullptr,
                           m, 2 * inter, hidden, num_experts, scale_major, gran_m, gran_n, gran_k, stream,
-                          "fp8_moe_fc1_silu_quant launch", q_out, q_scale_out);
+                          "fp8_moe_fc1_silu_quant launch", FP8G_OUT_BF16, q_out, q_scale_out);
   });
 }
 
 fp8g_status_t fp8_batch_gemm_masked(const void* a, const void* b, const float* a_scale,
                                     const float* b_scale, const int32_t* masked_m,
-                                    int64_t expected_m, void* out, int64_t num_groups,
-                                    int64_t max_m, int64_t n, int64_t k, int32_t scale_major,
-                                    int32_t gran_m, int32_t gran_n, int32_t gran_k, void* stream) {
+                                    int64_t expected_m, void* out, int32_t out_dtype,
+                                    int64_t num_groups, int64_t max_m, int64_t n, int64_t k,
+                                    int32_t scale_major, int32_t gran_m, int32_t gran_n,
+                                    int32_t gran_k, void* stream) {
   return guarded([&] {
     check_gemm_dims(max_m, n, k);
     require(num_groups >= 0 && num_groups <= 65535, "num_groups must be in [0, 65535]");
     require(expected_m >= 0, "expected_m must be non-negative");
     check_scale_major(scale_major);
     check_granularity(gran_m, gran_n, gran_k);
+    check_out_dtype(out_dtype);
     if (max_m == 0 || n == 0 || num_groups == 0) return;
     check_operands(a, b, a_scale, b_scale, out, k);
     require(masked_m != nullptr && aligned(masked_m, 4), "masked_m must be non-null and 4-byte aligned");
@@ -331,6 +342,7 @@ fp8g_status_t fp8_batch_gemm_masked(const void* a, const void* b, const float* a
     p.sa = a_scale;
     p.sb = b_scale;
     p.out = static_cast<uint16_t*>(out);
+    p.out_fp16 = out_dtype == FP8G_OUT_FP16;
     p.rowinfo = masked_m;
     p.m = (int32_t)max_m;
     p.n = (int32_t)n;

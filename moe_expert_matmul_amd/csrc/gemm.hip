@@ -402,7 +402,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     return;
   }
 
-  // ---- epilogue: BF16 round-to-nearest-even, 8-byte stores of valid rows ---------------------
+  // ---- epilogue: BF16 (or FP16) round-to-nearest-even, 8-byte stores of valid rows -----------
   if (wave_live) {
   uint16_t* O = p.out + (int64_t)g * p.out_group_stride;
   const int jl = (lane >> 4) * 4;
@@ -417,11 +417,18 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     for (int jg = 0; jg < T::JG; ++jg) {
       const int j = col0 + j0 + jg * 16 + jl;
       if (j >= p.n) continue;
-      const bf16x2 lo = {(__bf16)acc[ig][jg][0], (__bf16)acc[ig][jg][1]};
-      const bf16x2 hi = {(__bf16)acc[ig][jg][2], (__bf16)acc[ig][jg][3]};
       uint2 v;
-      v.x = __builtin_bit_cast(uint32_t, lo);
-      v.y = __builtin_bit_cast(uint32_t, hi);
+      if (p.out_fp16) {
+        const f16x2 lo = {(_Float16)acc[ig][jg][0], (_Float16)acc[ig][jg][1]};
+        const f16x2 hi = {(_Float16)acc[ig][jg][2], (_Float16)acc[ig][jg][3]};
+        v.x = __builtin_bit_cast(uint32_t, lo);
+        v.y = __builtin_bit_cast(uint32_t, hi);
+      } else {
+        const bf16x2 lo = {(__bf16)acc[ig][jg][0], (__bf16)acc[ig][jg][1]};
+        const bf16x2 hi = {(__bf16)acc[ig][jg][2], (__bf16)acc[ig][jg][3]};
+        v.x = __builtin_bit_cast(uint32_t, lo);
+        v.y = __builtin_bit_cast(uint32_t, hi);
+      }
       *reinterpret_cast<uint2*>(orow + j) = v;
     }
   }

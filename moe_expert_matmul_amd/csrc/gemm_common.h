@@ -10,6 +10,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int KBLK = 128;         // K-block width = bytes of one row per K block
 constexpr int SLAB_ROWS = 8;      // rows filled by one wave-wide 16-byte-per-lane LDS load

@@ -20,13 +20,14 @@ struct GemmParams {
   const uint8_t* b;
   const float* sa;
   const float* sb;
-  uint16_t* out;
+  uint16_t* out;           // BF16, or FP16 when out_fp16
   const int32_t* rowinfo;  // m_indices (CONTIG) or masked_m (MASKED)
   const int32_t* a_rows;   // CONTIG only: row r of the product takes row a_rows[r] of a; null: r
   int32_t a_src_rows;      // rows of a (and of a_scale) in memory
   // CONTIG_SWIGLU: b holds gate rows [0, inter) then up rows [inter, 2 inter); column tile t
   // computes gate and up of output columns [128 t, 128 t + 128) and writes
   // q_out[r][c] = E4M3(silu(gate) * up / q_scale_out[r][t]) with a 1x128 scale per row and tile.
+  int32_t out_fp16;
   int32_t inter;
   uint8_t* q_out;
   float* q_scale_out;

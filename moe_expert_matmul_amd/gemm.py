@@ -16,7 +16,12 @@ import torch
 from . import _lib
 
 _FP8_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+_OUT_DTYPES = (torch.bfloat16, torch.float16)  # out_dtype 0 and 1 of the C ABI
 _GRAN = (1, 128, 128)
+
+
+def _out_code(out: torch.Tensor) -> int:
+    return _OUT_DTYPES.index(out.dtype)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -55,7 +60,7 @@ def _require_cuda(a: torch.Tensor) -> torch.device:
 
 
 def fp8_gemm_nt_groupwise(a, b, a_scale, b_scale, out, scale_major="K", granularity=_GRAN) -> torch.Tensor:
-    """out (m,n) bf16 = a (m,k) @ b (n,k).T with 1x128 / 128x128 FP32 scales."""
+    """out (m,n) bf16 or fp16 = a (m,k) @ b (n,k).T with 1x128 / 128x128 FP32 scales."""
     dev = _require_cuda(a)
     m, k = a.shape
     n = b.shape[0]
@@ -65,10 +70,10 @@ def fp8_gemm_nt_groupwise(a, b, a_scale, b_scale, out, scale_major="K", granular
     _check(b, "b", _FP8_DTYPES, (n, k), dev)
     _check(a_scale, "a_scale", (torch.float32,), (m, kb) if major == 0 else (kb, m), dev)
     _check(b_scale, "b_scale", (torch.float32,), (nb, kb) if major == 0 else (kb, nb), dev)
-    _check(out, "out", (torch.bfloat16,), (m, n), dev)
+    _check(out, "out", _OUT_DTYPES, (m, n), dev)
     with torch.cuda.device(dev):
         st = _lib.load().fp8_gemm_nt_groupwise(_ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale), _ptr(out),
-                                               m, n, k, major, *granularity, _stream(dev))
+                                               _out_code(out), m, n, k, major, *granularity, _stream(dev))
     _lib.check(st, "fp8_gemm_nt_groupwise")
     return out
 
@@ -86,10 +91,11 @@ def fp8_group_gemm_contiguous(a, b, a_scale, b_scale, m_indices, out, scale_majo
     _check(a_scale, "a_scale", (torch.float32,), (m, kb) if major == 0 else (kb, m), dev)
     _check(b_scale, "b_scale", (torch.float32,), (groups, nb, kb) if major == 0 else (groups, kb, nb), dev)
     _check(m_indices, "m_indices", (torch.int32,), (m,), dev)
-    _check(out, "out", (torch.bfloat16,), (m, n), dev)
+    _check(out, "out", _OUT_DTYPES, (m, n), dev)
     with torch.cuda.device(dev):
         st = _lib.load().fp8_group_gemm_contiguous(_ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale), _ptr(m_indices),
-                                                   _ptr(out), m, n, k, groups, major, *granularity, _stream(dev))
+                                                   _ptr(out), _out_code(out), m, n, k, groups, major, *granularity,
+                                                   _stream(dev))
     _lib.check(st, "fp8_group_gemm_contiguous")
     return out
 
@@ -109,11 +115,11 @@ def fp8_group_gemm_contiguous_gather(a, a_scale, a_rows, b, b_scale, m_indices, 
     _check(b, "b", _FP8_DTYPES, (groups, n, k), dev)
     _check(b_scale, "b_scale", (torch.float32,), (groups, nb, kb) if major == 0 else (groups, kb, nb), dev)
     _check(m_indices, "m_indices", (torch.int32,), (m,), dev)
-    _check(out, "out", (torch.bfloat16,), (m, n), dev)
+    _check(out, "out", _OUT_DTYPES, (m, n), dev)
     with torch.cuda.device(dev):
         st = _lib.load().fp8_group_gemm_contiguous_gather(_ptr(a), _ptr(a_scale), rows_total, _ptr(a_rows), _ptr(b),
-                                                          _ptr(b_scale), _ptr(m_indices), _ptr(out), m, n, k, groups,
-                                                          major, *granularity, _stream(dev))
+                                                          _ptr(b_scale), _ptr(m_indices), _ptr(out), _out_code(out),
+                                                          m, n, k, groups, major, *granularity, _stream(dev))
     _lib.check(st, "fp8_group_gemm_contiguous_gather")
     return out
 
@@ -131,21 +137,24 @@ def fp8_batch_gemm_masked(a, b, a_scale, b_scale, masked_m, expected_m, out, sca
     _check(a_scale, "a_scale", (torch.float32,), (groups, max_m, kb) if major == 0 else (groups, kb, max_m), dev)
     _check(b_scale, "b_scale", (torch.float32,), (groups, nb, kb) if major == 0 else (groups, kb, nb), dev)
     _check(masked_m, "masked_m", (torch.int32,), (groups,), dev)
-    _check(out, "out", (torch.bfloat16,), (groups, max_m, n), dev)
+    _check(out, "out", _OUT_DTYPES, (groups, max_m, n), dev)
     with torch.cuda.device(dev):
         st = _lib.load().fp8_batch_gemm_masked(_ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale), _ptr(masked_m),
-                                               int(expected_m), _ptr(out), groups, max_m, n, k, major,
-                                               *granularity, _stream(dev))
+                                               int(expected_m), _ptr(out), _out_code(out), groups, max_m, n, k,
+                                               major, *granularity, _stream(dev))
     _lib.check(st, "fp8_batch_gemm_masked")
     return out
 
 
 def _out_dtype(out, out_dtype):
+    """dtype of the result: out's when given, else out_dtype (BF16 by default; BF16 or FP16)."""
     if out is not None:
         return out.dtype
-    if out_dtype not in (None, torch.bfloat16):
-        raise NotImplementedError("only BF16 output is implemented")
-    return torch.bfloat16
+    if out_dtype is None:
+        return torch.bfloat16
+    if out_dtype not in _OUT_DTYPES:
+        raise NotImplementedError(f"out_dtype {out_dtype} is not implemented (BF16 or FP16)")
+    return out_dtype
 
 
 def gemm_fp8_nt_groupwise(a: torch.Tensor, b: torch.Tensor, a_scale: torch.Tensor, b_scale: torch.Tensor,
@@ -160,7 +169,7 @@ def gemm_fp8_nt_groupwise(a: torch.Tensor, b: torch.Tensor, a_scale: torch.Tenso
         raise NotImplementedError("backend must be 'auto'")
     if output_scale is not None:
         raise NotImplementedError("FP8 output (output_scale) is not implemented")
-    _out_dtype(out, out_dtype)
+    dtype = _out_dtype(out, out_dtype)
     m, k = a.shape
     n = b.shape[0]
     major = _major(scale_major_mode)
@@ -168,7 +177,7 @@ def gemm_fp8_nt_groupwise(a: torch.Tensor, b: torch.Tensor, a_scale: torch.Tenso
         shape = (n // 128, k // 128) if major == 0 else (k // 128, n // 128)
         b_scale = b_scale.to(torch.float32).expand(shape).contiguous()
     if out is None:
-        out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+        out = torch.empty((m, n), dtype=dtype, device=a.device)
     return fp8_gemm_nt_groupwise(a, b, a_scale, b_scale, out, major, tuple(scale_granularity_mnk))
 
 
@@ -179,8 +188,7 @@ def group_deepgemm_fp8_nt_groupwise(a: torch.Tensor, b: torch.Tensor, a_scale: t
                                     out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
     """Contiguous grouped FP8 NT GEMM (K-major scales); padding rows of ``out`` are unspecified."""
     if out is None:
-        _out_dtype(None, out_dtype)
-        out = torch.empty((a.shape[0], b.shape[1]), dtype=torch.bfloat16, device=a.device)
+        out = torch.empty((a.shape[0], b.shape[1]), dtype=_out_dtype(None, out_dtype), device=a.device)
     return fp8_group_gemm_contiguous(a, b, a_scale, b_scale, m_indices, out, "K", tuple(scale_granularity_mnk))
 
 
@@ -191,7 +199,6 @@ def batch_deepgemm_fp8_nt_groupwise(a: torch.Tensor, b: torch.Tensor, a_scale: t
                                     out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
     """Masked batched FP8 NT GEMM (K-major scales); rows at or beyond masked_m[g] are unspecified."""
     if out is None:
-        _out_dtype(None, out_dtype)
-        out = torch.empty((a.shape[0], a.shape[1], b.shape[1]), dtype=torch.bfloat16, device=a.device)
+        out = torch.empty((a.shape[0], a.shape[1], b.shape[1]), dtype=_out_dtype(None, out_dtype), device=a.device)
     return fp8_batch_gemm_masked(a, b, a_scale, b_scale, masked_m, expected_m, out, "K",
                                  tuple(scale_granularity_mnk))

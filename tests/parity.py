@@ -47,11 +47,16 @@ def assert_within_tolerance(gpu: np.ndarray, ref: np.ndarray, what: str, rms=Non
                              f"(rms {rms:.4g}); first: {detail}")
 
 
-def sentinel_like(shape, device) -> torch.Tensor:
-    """BF16 buffer filled with a recognisable pattern (0x7FC1, a NaN) to detect stray writes."""
-    return torch.full(shape, 0x7FC1, dtype=torch.int16, device=device).view(torch.bfloat16)
+def fp16_values(t: torch.Tensor) -> np.ndarray:
+    """float64 values of an FP16 device tensor."""
+    return workloads.to_numpy(t).astype(np.float64)
+
+
+def sentinel_like(shape, device, dtype=torch.bfloat16) -> torch.Tensor:
+    """BF16 (or FP16) buffer filled with the bit pattern 0x7FC1 (a NaN in both) to detect stray writes."""
+    return torch.full(shape, 0x7FC1, dtype=torch.int16, device=device).view(dtype)
 
 
 def untouched(t: torch.Tensor) -> np.ndarray:
     """Boolean mask of the entries that still hold the sentinel."""
-    return workloads.to_numpy(t) == 0x7FC1
+    return t.detach().cpu().view(torch.int16).numpy() == 0x7FC1

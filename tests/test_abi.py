@@ -56,52 +56,59 @@ def _status(fn, *args):
 
 
 def test_plain_rejects_k_not_multiple_of_128(lib):
-    st, msg = _status(lib.fp8_gemm_nt_groupwise, P, P, P, P, P, 4, 128, 100, 0, *GRAN, None)
+    st, msg = _status(lib.fp8_gemm_nt_groupwise, P, P, P, P, P, 0, 4, 128, 100, 0, *GRAN, None)
     assert st == _lib.INVALID_ARGUMENT and "k (100)" in msg
 
 
 def test_plain_rejects_n_not_multiple_of_128(lib):
-    st, msg = _status(lib.fp8_gemm_nt_groupwise, P, P, P, P, P, 4, 200, 128, 0, *GRAN, None)
+    st, msg = _status(lib.fp8_gemm_nt_groupwise, P, P, P, P, P, 0, 4, 200, 128, 0, *GRAN, None)
     assert st == _lib.INVALID_ARGUMENT and "n (200)" in msg
 
 
 def test_plain_rejects_negative_sizes_and_bad_layout(lib):
-    assert lib.fp8_gemm_nt_groupwise(P, P, P, P, P, -1, 128, 128, 0, *GRAN, None) == _lib.INVALID_ARGUMENT
-    st, msg = _status(lib.fp8_gemm_nt_groupwise, P, P, P, P, P, 4, 128, 128, 7, *GRAN, None)
+    assert lib.fp8_gemm_nt_groupwise(P, P, P, P, P, 0, -1, 128, 128, 0, *GRAN, None) == _lib.INVALID_ARGUMENT
+    st, msg = _status(lib.fp8_gemm_nt_groupwise, P, P, P, P, P, 0, 4, 128, 128, 7, *GRAN, None)
     assert st == _lib.INVALID_ARGUMENT and "scale_major" in msg
 
 
 def test_unsupported_granularity_is_not_supported(lib):
-    st, msg = _status(lib.fp8_gemm_nt_groupwise, P, P, P, P, P, 4, 128, 128, 0, 1, 64, 128, None)
+    st, msg = _status(lib.fp8_gemm_nt_groupwise, P, P, P, P, P, 0, 4, 128, 128, 0, 1, 64, 128, None)
     assert st == _lib.NOT_SUPPORTED and "granularity" in msg
-    st, _ = _status(lib.fp8_group_gemm_contiguous, P, P, P, P, P, P, 128, 128, 128, 2, 0, 128, 128, 128, None)
+    st, _ = _status(lib.fp8_group_gemm_contiguous, P, P, P, P, P, P, 0, 128, 128, 128, 2, 0, 128, 128, 128, None)
     assert st == _lib.NOT_SUPPORTED
 
 
 def test_null_and_misaligned_pointers_are_rejected(lib):
-    st, msg = _status(lib.fp8_gemm_nt_groupwise, None, P, P, P, P, 4, 128, 128, 0, *GRAN, None)
+    st, msg = _status(lib.fp8_gemm_nt_groupwise, None, P, P, P, P, 0, 4, 128, 128, 0, *GRAN, None)
     assert st == _lib.INVALID_ARGUMENT and "non-null" in msg
-    st, msg = _status(lib.fp8_gemm_nt_groupwise, P, P, P, P, None, 4, 128, 0, 0, *GRAN, None)
+    st, msg = _status(lib.fp8_gemm_nt_groupwise, P, P, P, P, None, 0, 4, 128, 0, 0, *GRAN, None)
     assert st == _lib.INVALID_ARGUMENT and "out must be non-null" in msg
-    st, msg = _status(lib.fp8_gemm_nt_groupwise, ctypes.c_void_p(17), P, P, P, P, 4, 128, 128, 0, *GRAN, None)
+    st, msg = _status(lib.fp8_gemm_nt_groupwise, ctypes.c_void_p(17), P, P, P, P, 0, 4, 128, 128, 0, *GRAN, None)
     assert st == _lib.INVALID_ARGUMENT and "aligned" in msg
 
 
 def test_empty_problems_are_successful_no_ops(lib):
-    assert lib.fp8_gemm_nt_groupwise(None, None, None, None, None, 0, 128, 128, 0, *GRAN, None) == _lib.OK
-    assert lib.fp8_gemm_nt_groupwise(None, None, None, None, None, 5, 0, 128, 0, *GRAN, None) == _lib.OK
-    assert lib.fp8_batch_gemm_masked(None, None, None, None, None, 0, None, 0, 64, 128, 128, 0, *GRAN, None) == _lib.OK
-    assert lib.fp8_group_gemm_contiguous(None, None, None, None, None, None, 0, 128, 128, 4, 0, *GRAN, None) == _lib.OK
+    assert lib.fp8_gemm_nt_groupwise(None, None, None, None, None, 0, 0, 128, 128, 0, *GRAN, None) == _lib.OK
+    assert lib.fp8_gemm_nt_groupwise(None, None, None, None, None, 0, 5, 0, 128, 0, *GRAN, None) == _lib.OK
+    assert lib.fp8_batch_gemm_masked(None, None, None, None, None, 0, None, 0, 0, 64, 128, 128, 0, *GRAN, None) == _lib.OK
+    assert lib.fp8_group_gemm_contiguous(None, None, None, None, None, None, 0, 0, 128, 128, 4, 0, *GRAN, None) == _lib.OK
     assert lib.fp8g_last_error() == b""
 
 
 def test_contiguous_requires_128_row_multiple(lib):
-    st, msg = _status(lib.fp8_group_gemm_contiguous, P, P, P, P, P, P, 100, 128, 128, 2, 0, *GRAN, None)
+    st, msg = _status(lib.fp8_group_gemm_contiguous, P, P, P, P, P, P, 0, 100, 128, 128, 2, 0, *GRAN, None)
     assert st == _lib.INVALID_ARGUMENT and "multiple of 128" in msg
 
 
+def test_bad_out_dtype_is_rejected(lib):
+    st, msg = _status(lib.fp8_gemm_nt_groupwise, P, P, P, P, P, 2, 4, 128, 128, 0, *GRAN, None)
+    assert st == _lib.INVALID_ARGUMENT and "out_dtype" in msg
+    st, msg = _status(lib.fp8_batch_gemm_masked, P, P, P, P, P, 1, P, 7, 2, 64, 128, 128, 0, *GRAN, None)
+    assert st == _lib.INVALID_ARGUMENT and "out_dtype" in msg
+
+
 def test_masked_rejects_negative_expected_m(lib):
-    st, _ = _status(lib.fp8_batch_gemm_masked, P, P, P, P, P, -1, P, 2, 64, 128, 128, 0, *GRAN, None)
+    st, _ = _status(lib.fp8_batch_gemm_masked, P, P, P, P, P, -1, P, 0, 2, 64, 128, 128, 0, *GRAN, None)
     assert st == _lib.INVALID_ARGUMENT
 
 
@@ -118,9 +125,9 @@ def test_moe_steps_validate_sizes(lib):
 
 
 def test_error_message_is_cleared_by_the_next_successful_call(lib):
-    lib.fp8_gemm_nt_groupwise(P, P, P, P, P, 4, 128, 100, 0, *GRAN, None)
+    lib.fp8_gemm_nt_groupwise(P, P, P, P, P, 0, 4, 128, 100, 0, *GRAN, None)
     assert lib.fp8g_last_error() != b""
-    assert lib.fp8_gemm_nt_groupwise(None, None, None, None, None, 0, 128, 128, 0, *GRAN, None) == _lib.OK
+    assert lib.fp8_gemm_nt_groupwise(None, None, None, None, None, 0, 0, 128, 128, 0, *GRAN, None) == _lib.OK
     assert lib.fp8g_last_error() == b""
 
 

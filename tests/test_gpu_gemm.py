@@ -14,7 +14,7 @@ import torch
 import moe_expert_matmul_amd as fp8g
 import workloads
 from oracle import bf16, gemm as ogemm
-from parity import assert_within_tolerance, bf16_values, host, say, sentinel_like, untouched
+from parity import assert_within_tolerance, bf16_values, fp16_values, host, say, sentinel_like, untouched
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -80,6 +80,54 @@ def test_results_do_not_depend_on_the_tile_configuration(form):
     finally:
         os.environ.pop("FP8G_TILE", None)
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+@pytest.mark.parametrize("form", ["plain", "contiguous", "masked"])
+def test_fp16_output_matches_oracle(form):
+    """out_dtype FP16 (the page's other output type): same product, FP16 round-to-nearest-even."""
+    say("fp16 output", form)
+    if form == "plain":
+        d = workloads.plain(300, 640, 1024, seed=41, device=DEV)
+        out = sentinel_like((300, 640), DEV, torch.float16)
+        fp8g.fp8_gemm_nt_groupwise(d["a"], d["b"], d["a_scale"], d["b_scale"], out)
+        torch.cuda.synchronize()
+        assert_within_tolerance(fp16_values(out), _plain_ref(d), "plain fp16")
+        wrapped = fp8g.gemm_fp8_nt_groupwise(d["a"], d["b"], d["a_scale"], d["b_scale"], out_dtype=torch.float16)
+        torch.cuda.synchronize()
+        assert wrapped.dtype == torch.float16 and torch.equal(wrapped, out)
+    elif form == "contiguous":
+        d = workloads.contiguous(4, n=256, k=384, seed=42, device=DEV, counts=[130, 0, 5, 300])
+        out = sentinel_like((d["m"], d["n"]), DEV, torch.float16)
+        fp8g.fp8_group_gemm_contiguous(d["a"], d["b"], d["a_scale"], d["b_scale"], d["m_indices"], out)
+        torch.cuda.synchronize()
+        assert_within_tolerance(fp16_values(out), _contig_ref(d), "contiguous fp16")
+        mi = host(d["m_indices"])
+        assert untouched(out)[mi < 0].all() and not untouched(out)[mi >= 0].any()
+    else:
+        mm = np.array([0, 200, 77, 129], np.int32)
+        d = workloads.masked(4, 200, 384, 512, 128, seed=43, device=DEV, masked_m=mm)
+        out = sentinel_like((4, 200, 384), DEV, torch.float16)
+        fp8g.fp8_batch_gemm_masked(d["a"], d["b"], d["a_scale"], d["b_scale"], d["masked_m"], 128, out)
+        torch.cuda.synchronize()
+        assert_within_tolerance(fp16_values(out), _masked_ref(d, mm), "masked fp16")
+
+
+def test_fp16_output_overflows_to_inf():
+    """448 * 448 * 128 = 25.7e6 is beyond FP16's 65504: the output is +inf (and -inf), as the
+    oracle's FP16 rounding of the exact value gives."""
+    say("fp16 overflow")
+    k = 128
+    a = torch.full((4, k), 0x7E, dtype=torch.uint8, device=DEV)  # +448
+    b = torch.full((128, k), 0x7E, dtype=torch.uint8, device=DEV)
+    b[64:] = 0xFE  # -448
+    sa = torch.ones((4, 1), device=DEV)
+    sb = torch.ones((1, 1), device=DEV)
+    out = fp8g.gemm_fp8_nt_groupwise(a, b, sa, sb, out_dtype=torch.float16)
+    torch.cuda.synchronize()
+    with np.errstate(over="ignore"):  # the overflow to inf is the point
+        ref = ogemm.gemm_fp8_nt_groupwise(host(a), host(b), host(sa), host(sb)).astype(np.float16)
+    got = fp16_values(out)
+    assert np.isinf(ref).all() and np.array_equal(got, ref.astype(np.float64))
 
 
 def test_plain_full_size_sampled_rows():
