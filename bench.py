@@ -11,8 +11,8 @@ kernel source, else null. ``cpu_baseline`` times the float64 CPU oracle on a bou
 the same workload.
 
 --configs adds the other workloads (contiguous grouped over 32 Zipf-sized experts, masked batched
-over 16 groups, the 4096-token expert FFN), each timed per launch with the caches flushed in
-between, under "configs".
+over 16 groups, the add-RMSNorm + 1x128 quantiser and the plain quantiser over 4096x7168 BF16, the
+4096-token expert FFN), each timed per launch with the caches flushed in between, under "configs".
 """
 
 from __future__ import annotations
@@ -153,6 +153,26 @@ def other_configs(steps, warmup):
         "hbm_gbs": round(hbm / med / 1e6, 1), "frac_hbm": round(hbm / med / 1e6 / HBM_PEAK_GBS, 4),
         "frac_mfma": round(flops / med / 1e9 / FP8_DENSE_PEAK_TFLOPS, 4), "sum_masked_m": int(mm.sum())}
     del d, out
+
+    d = workloads.norm(4096, 7168, seed=0, device=dev)
+    res_t = d["residual"].clone()
+    normed = torch.empty_like(d["input"])
+    q = torch.empty((4096, 7168), dtype=torch.uint8, device=dev)
+    qs = torch.empty((4096, 56), dtype=torch.float32, device=dev)
+    fn = lambda: fp8g.fused_add_rmsnorm_fp8_block_quant(q, qs, normed, d["input"], res_t, d["weight"])
+    med, best = time_cold(fn, steps, warmup, flush)
+    # reads input + residual (2 B each), writes residual + normed_out (2 B each), codes (1 B), scales
+    hbm = 4096 * 7168 * 9 + 4096 * 56 * 4 + 7168 * 2
+    res["add_rmsnorm_quant_4096x7168"] = {
+        "ms": round(med, 4), "ms_best": round(best, 4), "hbm_gbs": round(hbm / med / 1e6, 1),
+        "frac_hbm": round(hbm / med / 1e6 / HBM_PEAK_GBS, 4)}
+    fn = lambda: fp8g.fp8_quantize_1x128(d["input"], q, qs)
+    med, best = time_cold(fn, steps, warmup, flush)
+    hbm = 4096 * 7168 * 3 + 4096 * 56 * 4
+    res["quantize_1x128_4096x7168"] = {
+        "ms": round(med, 4), "ms_best": round(best, 4), "hbm_gbs": round(hbm / med / 1e6, 1),
+        "frac_hbm": round(hbm / med / 1e6 / HBM_PEAK_GBS, 4)}
+    del d, res_t, normed, q, qs
 
     d = workloads.moe(seed=0, device=dev)
     ws = fp8g.MoeWorkspace.allocate(4096, 8, 64, 7168, 2048, dev)

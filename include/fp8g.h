@@ -151,6 +151,40 @@ FP8G_API fp8g_status_t fp8_batch_gemm_masked(const void* a, const void* b, const
                                     int32_t gran_m, int32_t gran_n, int32_t gran_k, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Producers of the a operand (1x128 E4M3 rows with FP32 scales).
+ * ------------------------------------------------------------------------------------------- */
+
+/*
+ * 1x128 activation quantiser: for every row r and 128-column block c of x,
+ *   scale[r][c] = amax / 448 (FP32 IEEE division; 1 when the block is all zero)
+ *   out[r][c*128 + t] = E4M3_RNE(x[r][c*128 + t] / scale[r][c])   (FP32 IEEE division)
+ * The a_scale layout of the MATE FlashInfer-API page (section "GEMM"): K-major (rows, cols/128) or
+ * MN-major (cols/128, rows).
+ *   x         (rows, cols) BF16; out (rows, cols) E4M3; scale_out FP32 in scale_major layout
+ * cols must be a multiple of 128.
+ */
+FP8G_API fp8g_status_t fp8_quantize_1x128(const void* x, int64_t rows, int64_t cols, void* out,
+                                 float* scale_out, int32_t scale_major, void* stream);
+
+/*
+ * Fused add-RMSNorm with 1x128 FP8 quantisation (MATE FlashInfer-API page, section "norm",
+ * fused_add_rmsnorm_fp8_block_quant; arguments in its order):
+ *   residual[r]   <- bf16(input[r] + residual[r])                 (in place; FP32 sum, RNE)
+ *   normed_out[r] <- bf16(residual[r] * (1/sqrt(mean_j residual[r][j]^2 + eps)) * weight)
+ *   out[r], block_scale[r]  <- the 1x128 quantisation above of normed_out[r]
+ * All arithmetic is FP32 (the mean is an FP32 sum of squares over hidden divided by hidden).
+ *   input, residual, normed_out  (rows, hidden) BF16;  weight (hidden,) BF16
+ *   out (rows, hidden) E4M3;  block_scale FP32, (rows, hidden/128) K-major or (hidden/128, rows)
+ *   MN-major
+ * hidden must be a multiple of 128; normed_out may be input; residual must be distinct from the
+ * other tensors.
+ */
+FP8G_API fp8g_status_t fp8_fused_add_rmsnorm_quant(void* out, float* block_scale, void* normed_out,
+                                          const void* input, void* residual, const void* weight,
+                                          float eps, int64_t rows, int64_t hidden,
+                                          int32_t scale_major, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Expert-FFN steps around the grouped GEMM (flashinfer-rs README, section "API Example: Fused MoE
  * FP8 (cudarc)", DeepSeek FP8 block-scale mode: BF16 tokens, int32 token_selected
  * (num_tokens, top_k), fc1 weights (num_experts, 2*inter, hidden) holding gate then up rows, fc2

@@ -25,3 +25,4 @@ from .moe import (  # noqa: F401
     moe_gather_quant,
     moe_silu_mul_quant,
 )
+from .quant import fp8_quantize_1x128, fused_add_rmsnorm_fp8_block_quant  # noqa: F401

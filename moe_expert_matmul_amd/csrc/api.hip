@@ -416,6 +416,51 @@ fp8g_status_t fp8_moe_gather_quant(const void* x, const int32_t* src_token, int6
   });
 }
 
+fp8g_status_t fp8_quantize_1x128(const void* x, int64_t rows, int64_t cols, void* out, float* scale_out,
+                                 int32_t scale_major, void* stream) {
+  return guarded([&] {
+    require(rows >= 0 && cols >= 0, "sizes must be non-negative");
+    require(cols % 128 == 0, "cols (%lld) must be a multiple of 128", (long long)cols);
+    require(rows <= kInt32Max && cols <= kInt32Max && rows * cols <= (int64_t)1 << 40, "sizes too large");
+    check_scale_major(scale_major);
+    if (rows == 0 || cols == 0) return;
+    require(x && out && scale_out, "pointers must be non-null");
+    require(aligned(x, 16) && aligned(out, 16) && aligned(scale_out, 4),
+            "x and out must be 16-byte aligned, scale_out 4-byte aligned");
+    check_device();
+    check_hip(fp8g::launch_quantize_1x128(static_cast<const uint16_t*>(x), (int)rows, (int)cols,
+                                          static_cast<uint8_t*>(out), scale_out, scale_major == FP8G_SCALE_MN_MAJOR,
+                                          (hipStream_t)stream),
+              "fp8_quantize_1x128 launch");
+  });
+}
+
+fp8g_status_t fp8_fused_add_rmsnorm_quant(void* out, float* block_scale, void* normed_out, const void* input,
+                                          void* residual, const void* weight, float eps, int64_t rows,
+                                          int64_t hidden, int32_t scale_major, void* stream) {
+  return guarded([&] {
+    require(rows >= 0 && hidden >= 0, "sizes must be non-negative");
+    require(hidden % 128 == 0, "hidden (%lld) must be a multiple of 128", (long long)hidden);
+    require(rows <= kInt32Max && hidden <= kInt32Max && rows * hidden <= (int64_t)1 << 40, "sizes too large");
+    require(eps >= 0.0f && eps < INFINITY, "eps must be finite and non-negative");
+    check_scale_major(scale_major);
+    if (rows == 0 || hidden == 0) return;
+    require(out && block_scale && normed_out && input && residual && weight, "pointers must be non-null");
+    require(aligned(out, 16) && aligned(normed_out, 16) && aligned(input, 16) && aligned(residual, 16) &&
+                aligned(weight, 16) && aligned(block_scale, 4),
+            "tensors must be 16-byte aligned, block_scale 4-byte aligned");
+    require(residual != input && residual != normed_out && residual != weight,
+            "residual must not alias input, normed_out or weight");
+    check_device();
+    check_hip(fp8g::launch_fused_add_rmsnorm_quant(
+                  static_cast<const uint16_t*>(input), static_cast<uint16_t*>(residual),
+                  static_cast<const uint16_t*>(weight), eps, (int)rows, (int)hidden,
+                  static_cast<uint16_t*>(normed_out), static_cast<uint8_t*>(out), block_scale,
+                  scale_major == FP8G_SCALE_MN_MAJOR, (hipStream_t)stream),
+              "fp8_fused_add_rmsnorm_quant launch");
+  });
+}
+
 fp8g_status_t fp8_moe_silu_mul_quant(const void* y, const int32_t* m_indices, int64_t rows,
                                      int64_t inter, void* a_out, float* a_scale_out,
                                      void* stream) {

@@ -59,6 +59,12 @@ int tile_cols(TileConfig cfg);
 
 hipError_t launch_gemm(GemmMode mode, TileConfig cfg, GemmParams p, int grid, hipStream_t stream);
 
+hipError_t launch_quantize_1x128(const uint16_t* x, int rows, int cols, uint8_t* out, float* scale_out,
+                                 bool mn_major, hipStream_t stream);
+hipError_t launch_fused_add_rmsnorm_quant(const uint16_t* input, uint16_t* residual, const uint16_t* weight,
+                                          float eps, int rows, int hidden, uint16_t* normed_out, uint8_t* out,
+                                          float* scale_out, bool mn_major, hipStream_t stream);
+
 hipError_t launch_moe_build_permutation(const int32_t* topk_ids, int num_tokens, int top_k,
                                         int num_experts, int m_alloc, int32_t* m_indices,
                                         int32_t* src_token, int32_t* row_of_entry,

@@ -137,3 +137,22 @@ def test_python_binding_refuses_cpu_tensors():
     a = torch.zeros((4, 128), dtype=torch.uint8)
     with pytest.raises(ValueError):
         gemm_fp8_nt_groupwise(a, a, torch.ones(4, 1), torch.ones(1, 1))
+
+
+def test_producers_validate_arguments(lib):
+    st, msg = _status(lib.fp8_quantize_1x128, P, 4, 100, P, P, 0, None)
+    assert st == _lib.INVALID_ARGUMENT and "cols (100)" in msg
+    assert lib.fp8_quantize_1x128(None, 0, 256, None, None, 0, None) == _lib.OK
+    f = lib.fp8_fused_add_rmsnorm_quant
+    Q = ctypes.c_void_p(32)
+    st, msg = _status(f, P, P, P, P, Q, P, 1e-6, 4, 100, 0, None)
+    assert st == _lib.INVALID_ARGUMENT and "hidden (100)" in msg
+    st, msg = _status(f, P, P, P, Q, Q, P, 1e-6, 4, 128, 0, None)
+    assert st == _lib.INVALID_ARGUMENT and "alias" in msg
+    st, msg = _status(f, P, P, P, P, Q, P, -1.0, 4, 128, 0, None)
+    assert st == _lib.INVALID_ARGUMENT and "eps" in msg
+    st, msg = _status(f, P, P, P, P, Q, P, float("nan"), 4, 128, 0, None)
+    assert st == _lib.INVALID_ARGUMENT and "eps" in msg
+    st, msg = _status(f, P, P, P, P, Q, P, 1e-6, 4, 128, 3, None)
+    assert st == _lib.INVALID_ARGUMENT and "scale_major" in msg
+    assert f(None, None, None, None, None, None, 1e-6, 0, 7168, 0, None) == _lib.OK

@@ -15,6 +15,8 @@ Workloads (all seed-fixed):
   moe          router logits ~ N(0,1) (T,E); p = softmax; top-k by p (ties -> lower expert index);
                weights = p at the chosen experts (not renormalised); X ~ N(0,1) in BF16;
                W1 (E, 2I, H) and W2 (E, H, I) ~ N(0,1) quantised per 128x128 block.
+  norm         add-RMSNorm input ~ N(0,1), residual ~ N(0,1) times a per-row log-uniform scale,
+               weight ~ U(0.5, 1.5), all BF16.
 
 Small structural draws (sizes, counts, logits) use numpy's default_rng(seed); bulk tensors use a
 torch.Generator seeded with the same seed on the target device, so that full-size inputs are
@@ -136,6 +138,17 @@ def moe(num_tokens: int = 4096, hidden: int = 7168, num_experts: int = 64, top_k
     return dict(x=x, topk_ids=torch.from_numpy(ids).to(device), topk_weights=torch.from_numpy(w).to(device),
                 w1=w1, s1=s1, w2=w2, s2=s2, num_tokens=num_tokens, hidden=hidden,
                 num_experts=num_experts, top_k=top_k, inter=inter)
+
+
+def norm(rows: int = 4096, hidden: int = 7168, seed: int = 0, device="cpu"):
+    """Add-RMSNorm inputs: input ~ N(0,1), residual ~ N(0,1) * row scale (row scales log-uniform on
+    [1/8, 8], a residual stream whose rows differ in size), weight ~ U(0.5, 1.5); all BF16."""
+    g = _gen(seed, device)
+    row_scale = torch.from_numpy(np.exp2(np.random.default_rng(seed).uniform(-3, 3, (rows, 1)))).float().to(device)
+    inp = _normal((rows, hidden), g, device).to(torch.bfloat16)
+    res = (_normal((rows, hidden), g, device) * row_scale).to(torch.bfloat16)
+    w = (torch.rand(hidden, generator=g, device=device) + 0.5).to(torch.bfloat16)
+    return dict(input=inp, residual=res, weight=w, rows=rows, hidden=hidden)
 
 
 def to_numpy(t: torch.Tensor) -> np.ndarray:
