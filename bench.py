@@ -12,7 +12,8 @@ the same workload.
 
 --configs adds the other workloads (contiguous grouped over 32 Zipf-sized experts, masked batched
 over 16 groups, the add-RMSNorm + 1x128 quantiser and the plain quantiser over 4096x7168 BF16, the
-4096-token expert FFN), each timed per launch with the caches flushed in between, under "configs".
+4096-token expert FFN), each timed per launch with the caches evicted in between by a 512 MB read,
+under "configs".
 """
 
 from __future__ import annotations
@@ -72,7 +73,7 @@ def time_back_to_back(fn, steps: int, warmup: int):
 
 
 def time_cold(fn, steps: int, warmup: int, flush):
-    """Median per-launch time with a cache-flushing write between launches (not timed)."""
+    """Median per-launch time with a cache-evicting read between launches (not timed)."""
     import torch
     for _ in range(warmup):
         fn()
@@ -122,8 +123,10 @@ def other_configs(steps, warmup):
     import moe_expert_matmul_amd as fp8g
     import workloads
     dev = torch.device("cuda")
-    scratch = torch.empty(1 << 29, dtype=torch.uint8, device=dev)  # 512 MB: evicts L2 and the MALL
-    flush = lambda: scratch.fill_(1)
+    # Reading 512 MB evicts L2 and the Infinity Cache. A write would leave dirty lines whose write-back
+    # then overlaps the timed launch (it cost the HBM-bound kernels up to a third of their time).
+    scratch = torch.ones(1 << 29, dtype=torch.uint8, device=dev)
+    flush = lambda: torch.amax(scratch)
     res = {}
 
     d = workloads.contiguous(32, 8192, 4096, 7168, 1.1, seed=0, device=dev)

@@ -77,15 +77,31 @@ FP8G_API int32_t fp8g_version(void);
  *   a        (m, k)  E4M3, row-major
  *   b        (n, k)  E4M3, row-major (the product is a @ b.T)
  *   a_scale  FP32, (m, k/128) when scale_major = K-major, (k/128, m) when MN-major
- *   b_scale  FP32, (n/128, k/128) when K-major, (k/128, n/128) when MN-major
+ *   b_scale  FP32, (NB, k/128) when K-major, (k/128, NB) when MN-major, NB = ceil(n/128)
  *   out      (m, n)  BF16 or FP16 (out_dtype), fully written
- * m >= 0 is arbitrary; n and k are multiples of 128. m == 0 or n == 0 is a no-op; k == 0 writes
- * zeros. scale_major applies to both scale tensors.
+ * m >= 0 and n >= 0 are arbitrary (output column j uses b-scale block j/128, so the last block may
+ * cover fewer than 128 rows of b); k is a multiple of 128. m == 0 or n == 0 is a no-op; k == 0
+ * writes zeros. scale_major applies to both scale tensors.
  */
 FP8G_API fp8g_status_t fp8_gemm_nt_groupwise(const void* a, const void* b, const float* a_scale,
                                     const float* b_scale, void* out, int32_t out_dtype, int64_t m,
                                     int64_t n, int64_t k, int32_t scale_major, int32_t gran_m,
                                     int32_t gran_n, int32_t gran_k, void* stream);
+
+/*
+ * Plain form with FP8 output: gemm_fp8_nt_groupwise's output_scale (MATE FlashInfer-API page,
+ * section "GEMM"), an FP32 scale for E4M3 output. Read here as one per-tensor dequantisation
+ * scale s = output_scale[0] (a device pointer):
+ *   out[i][j] = E4M3_RNE(saturate(acc[i][j] / s))   (FP32 IEEE division; beyond +-448 the code
+ *                                                    is +-448, NaN stays NaN)
+ * where acc is the FP32 value the plain form would round to BF16. Arguments and sizes as for
+ * fp8_gemm_nt_groupwise; out (m, n) holds E4M3 codes.
+ */
+FP8G_API fp8g_status_t fp8_gemm_nt_groupwise_fp8_out(const void* a, const void* b, const float* a_scale,
+                                            const float* b_scale, void* out,
+                                            const float* output_scale, int64_t m, int64_t n,
+                                            int64_t k, int32_t scale_major, int32_t gran_m,
+                                            int32_t gran_n, int32_t gran_k, void* stream);
 
 /*
  * Contiguous grouped form: out[i] = a[i] @ b[m_indices[i]].T for every row with m_indices[i] >= 0.

@@ -10,6 +10,7 @@ from .gemm import (  # noqa: F401
     batch_deepgemm_fp8_nt_groupwise,
     fp8_batch_gemm_masked,
     fp8_gemm_nt_groupwise,
+    fp8_gemm_nt_groupwise_fp8_out,
     fp8_group_gemm_contiguous,
     fp8_group_gemm_contiguous_gather,
     gemm_fp8_nt_groupwise,

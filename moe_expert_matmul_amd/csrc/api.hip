@@ -108,11 +108,13 @@ fp8g_status_t guarded(F&& body) {
 }
 
 // Shapes shared by the three GEMM forms.
-void check_gemm_dims(int64_t rows, int64_t n, int64_t k) {
+// n_tail: the plain form takes any n (the last b-scale block then covers fewer than 128 rows of b);
+// the grouped and masked forms need whole 128-row blocks.
+void check_gemm_dims(int64_t rows, int64_t n, int64_t k, bool n_tail = false) {
   require(rows >= 0 && n >= 0 && k >= 0, "sizes must be non-negative (rows %lld, n %lld, k %lld)",
           (long long)rows, (long long)n, (long long)k);
   require(k % 128 == 0, "k (%lld) must be a multiple of 128", (long long)k);
-  require(n % 128 == 0, "n (%lld) must be a multiple of 128", (long long)n);
+  require(n_tail || n % 128 == 0, "n (%lld) must be a multiple of 128", (long long)n);
   require(rows <= kInt32Max && n <= kInt32Max && k <= kInt32Max, "sizes must fit in int32");
   require(rows * k <= kUint32Max && n * k <= kUint32Max, "one operand matrix must stay below 4 GiB");
   require(rows * (k / 128) <= kInt32Max, "a_scale must have fewer than 2^31 elements per group");
@@ -161,41 +163,69 @@ const char* fp8g_last_error(void) { return g_last_error.c_str(); }
 
 int32_t fp8g_version(void) { return 100; }  // 0.1.0
 
+}  // extern "C"
+
+namespace {
+
+// The plain form for both output kinds: 16-bit (out_dtype) or E4M3 with out_scale.
+void plain_gemm(const void* a, const void* b, const float* a_scale, const float* b_scale, void* out,
+                int32_t out_dtype, const float* out_scale, int64_t m, int64_t n, int64_t k, int32_t scale_major,
+                int32_t gran_m, int32_t gran_n, int32_t gran_k, void* stream, const char* what) {
+  check_gemm_dims(m, n, k, /*n_tail=*/true);
+  check_scale_major(scale_major);
+  check_granularity(gran_m, gran_n, gran_k);
+  if (out_scale == nullptr) check_out_dtype(out_dtype);
+  if (m == 0 || n == 0) return;
+  check_operands(a, b, a_scale, b_scale, out, k);
+  check_device();
+  fp8g::GemmParams p{};
+  p.a = static_cast<const uint8_t*>(a);
+  p.b = static_cast<const uint8_t*>(b);
+  p.sa = a_scale;
+  p.sb = b_scale;
+  p.out = static_cast<uint16_t*>(out);
+  p.out_fp16 = out_dtype == FP8G_OUT_FP16;
+  p.out_scale = out_scale;
+  p.m = (int32_t)m;
+  p.n = (int32_t)n;
+  p.k = (int32_t)k;
+  p.kblocks = (int32_t)(k / 128);
+  p.nblocks = (int32_t)ceil_div(n, 128);
+  p.num_groups = 1;
+  p.a_src_rows = (int32_t)m;
+  set_scale_strides(p, scale_major, m);
+  fp8g::TileConfig cfg = m > 128 ? fp8g::TILE_256x256 : fp8g::TILE_128x256;
+  if (fp8g::tile_override() >= 0) cfg = (fp8g::TileConfig)fp8g::tile_override();
+  p.tiles_m = (int32_t)ceil_div(m, fp8g::tile_rows(cfg));
+  p.tiles_n = (int32_t)ceil_div(n, fp8g::tile_cols(cfg));
+  p.group_m = 4;
+  const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
+  check_hip(fp8g::launch_gemm(fp8g::MODE_PLAIN, cfg, p, (int)grid, (hipStream_t)stream), what);
+}
+
+}  // namespace
+
+extern "C" {
+
 fp8g_status_t fp8_gemm_nt_groupwise(const void* a, const void* b, const float* a_scale,
                                     const float* b_scale, void* out, int32_t out_dtype, int64_t m,
                                     int64_t n, int64_t k, int32_t scale_major, int32_t gran_m,
                                     int32_t gran_n, int32_t gran_k, void* stream) {
   return guarded([&] {
-    check_gemm_dims(m, n, k);
-    check_scale_major(scale_major);
-    check_granularity(gran_m, gran_n, gran_k);
-    check_out_dtype(out_dtype);
-    if (m == 0 || n == 0) return;
-    check_operands(a, b, a_scale, b_scale, out, k);
-    check_device();
-    fp8g::GemmParams p{};
-    p.a = static_cast<const uint8_t*>(a);
-    p.b = static_cast<const uint8_t*>(b);
-    p.sa = a_scale;
-    p.sb = b_scale;
-    p.out = static_cast<uint16_t*>(out);
-    p.out_fp16 = out_dtype == FP8G_OUT_FP16;
-    p.m = (int32_t)m;
-    p.n = (int32_t)n;
-    p.k = (int32_t)k;
-    p.kblocks = (int32_t)(k / 128);
-    p.nblocks = (int32_t)(n / 128);
-    p.num_groups = 1;
-    p.a_src_rows = (int32_t)m;
-    set_scale_strides(p, scale_major, m);
-    fp8g::TileConfig cfg = m > 128 ? fp8g::TILE_256x256 : fp8g::TILE_128x256;
-    if (fp8g::tile_override() >= 0) cfg = (fp8g::TileConfig)fp8g::tile_override();
-    p.tiles_m = (int32_t)ceil_div(m, fp8g::tile_rows(cfg));
-    p.tiles_n = (int32_t)ceil_div(n, fp8g::tile_cols(cfg));
-    p.group_m = 4;
-    const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
-    check_hip(fp8g::launch_gemm(fp8g::MODE_PLAIN, cfg, p, (int)grid, (hipStream_t)stream),
-              "fp8_gemm_nt_groupwise launch");
+    plain_gemm(a, b, a_scale, b_scale, out, out_dtype, nullptr, m, n, k, scale_major, gran_m, gran_n, gran_k, stream,
+               "fp8_gemm_nt_groupwise launch");
+  });
+}
+
+fp8g_status_t fp8_gemm_nt_groupwise_fp8_out(const void* a, const void* b, const float* a_scale,
+                                            const float* b_scale, void* out, const float* output_scale,
+                                            int64_t m, int64_t n, int64_t k, int32_t scale_major,
+                                            int32_t gran_m, int32_t gran_n, int32_t gran_k, void* stream) {
+  return guarded([&] {
+    require(output_scale != nullptr, "output_scale must be non-null");
+    require(aligned(output_scale, 4), "output_scale must be 4-byte aligned");
+    plain_gemm(a, b, a_scale, b_scale, out, FP8G_OUT_BF16, output_scale, m, n, k, scale_major, gran_m, gran_n,
+               gran_k, stream, "fp8_gemm_nt_groupwise_fp8_out launch");
   });
 }
 
@@ -404,6 +434,7 @@ fp8g_status_t fp8_moe_gather_quant(const void* x, const int32_t* src_token, int6
     require(hidden % 128 == 0, "hidden (%lld) must be a multiple of 128", (long long)hidden);
     require(m_alloc <= kInt32Max && hidden <= kInt32Max && num_tokens <= kInt32Max, "sizes must fit in int32");
     require(src_token != nullptr || m_alloc <= num_tokens, "without src_token, m_alloc must not exceed num_tokens");
+    require(m_alloc * (hidden / 128) < (int64_t)1 << 31, "m_alloc * hidden / 128 must be below 2^31");
     if (m_alloc == 0 || hidden == 0) return;
     require(x && a_out && a_scale_out, "pointers must be non-null");
     require(aligned(x, 16) && aligned(a_out, 16) && aligned(a_scale_out, 4) && aligned(src_token, 4),
@@ -421,7 +452,7 @@ fp8g_status_t fp8_quantize_1x128(const void* x, int64_t rows, int64_t cols, void
   return guarded([&] {
     require(rows >= 0 && cols >= 0, "sizes must be non-negative");
     require(cols % 128 == 0, "cols (%lld) must be a multiple of 128", (long long)cols);
-    require(rows <= kInt32Max && cols <= kInt32Max && rows * cols <= (int64_t)1 << 40, "sizes too large");
+    require(rows <= kInt32Max && cols <= kInt32Max && rows * (cols / 128) < (int64_t)1 << 31, "sizes too large");
     check_scale_major(scale_major);
     if (rows == 0 || cols == 0) return;
     require(x && out && scale_out, "pointers must be non-null");

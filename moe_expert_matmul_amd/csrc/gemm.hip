@@ -66,6 +66,8 @@ struct Tile {
 
 __device__ __forceinline__ float bf16_round(float x) { return (float)(__bf16)x; }  // RNE
 
+constexpr float kE4M3MaxOut = 448.0f;  // largest finite E4M3FN value
+
 // Epilogue of the expert FFN's fc1 (CONTIG_SWIGLU): the values the unfused path would store in
 // BF16 -- gate and up of each output column -- are rounded to BF16 here too, then
 // h = silu(gate) * up with silu(g) = g / (1 + exp(-g)) in FP32, and each row's 128 h values of the
@@ -402,10 +404,44 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     return;
   }
 
-  // ---- epilogue: BF16 (or FP16) round-to-nearest-even, 8-byte stores of valid rows -----------
+  // ---- epilogue: BF16 or FP16 round-to-nearest-even (8-byte stores), or E4M3 codes (4-byte
+  // stores) when the plain form has an output scale; valid rows and columns only. A lane holds 4
+  // consecutive columns; when n is not a multiple of 4 the row starts lose that alignment and each
+  // column is stored on its own.
   if (wave_live) {
-  uint16_t* O = p.out + (int64_t)g * p.out_group_stride;
   const int jl = (lane >> 4) * 4;
+  const bool vec = (p.n & 3) == 0;
+  if (MODE == MODE_PLAIN && p.out_scale != nullptr) {
+    const float so = *p.out_scale;
+    uint8_t* O = reinterpret_cast<uint8_t*>(p.out);
+#pragma unroll
+    for (int ig = 0; ig < T::IG; ++ig) {
+      const int i = row0 + i0 + ig * 16 + fr;
+      if (i >= row_end) continue;
+      uint8_t* orow = O + (int64_t)i * p.n;
+#pragma unroll
+      for (int jg = 0; jg < T::JG; ++jg) {
+        const int j = col0 + j0 + jg * 16 + jl;
+        if (j >= p.n) continue;
+        float q[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          q[r] = __fdiv_rn(acc[ig][jg][r], so);
+          if (!(fabsf(q[r]) <= kE4M3MaxOut) && q[r] == q[r]) q[r] = copysignf(kE4M3MaxOut, q[r]);  // saturate; NaN stays
+        }
+        int w4 = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+        w4 = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w4, true);
+        if (vec) {
+          *reinterpret_cast<int*>(orow + j) = w4;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (j + r < p.n) orow[j + r] = (uint8_t)((uint32_t)w4 >> (8 * r));
+        }
+      }
+    }
+  } else {
+  uint16_t* O = p.out + (int64_t)g * p.out_group_stride;
 #pragma unroll
   for (int ig = 0; ig < T::IG; ++ig) {
     const int i = row0 + i0 + ig * 16 + fr;
@@ -429,9 +465,17 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
         v.x = __builtin_bit_cast(uint32_t, lo);
         v.y = __builtin_bit_cast(uint32_t, hi);
       }
-      *reinterpret_cast<uint2*>(orow + j) = v;
+      if (vec) {
+        *reinterpret_cast<uint2*>(orow + j) = v;
+      } else {
+        const uint16_t e[4] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y, (uint16_t)(v.y >> 16)};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (j + r < p.n) orow[j + r] = e[r];
+      }
     }
   }
+  }  // 16-bit output
   }  // wave_live
 }
 

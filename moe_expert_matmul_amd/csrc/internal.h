@@ -20,7 +20,7 @@ struct GemmParams {
   const uint8_t* b;
   const float* sa;
   const float* sb;
-  uint16_t* out;           // BF16, or FP16 when out_fp16
+  uint16_t* out;           // BF16, or FP16 when out_fp16; E4M3 bytes when out_scale is set
   const int32_t* rowinfo;  // m_indices (CONTIG) or masked_m (MASKED)
   const int32_t* a_rows;   // CONTIG only: row r of the product takes row a_rows[r] of a; null: r
   int32_t a_src_rows;      // rows of a (and of a_scale) in memory
@@ -28,6 +28,8 @@ struct GemmParams {
   // computes gate and up of output columns [128 t, 128 t + 128) and writes
   // q_out[r][c] = E4M3(silu(gate) * up / q_scale_out[r][t]) with a 1x128 scale per row and tile.
   int32_t out_fp16;
+  // PLAIN only: E4M3 output, out[i][j] = E4M3_RNE(saturate(acc / out_scale[0])); null: 16-bit output
+  const float* out_scale;
   int32_t inter;
   uint8_t* q_out;
   float* q_scale_out;
@@ -59,6 +61,8 @@ int tile_cols(TileConfig cfg);
 
 hipError_t launch_gemm(GemmMode mode, TileConfig cfg, GemmParams p, int grid, hipStream_t stream);
 
+hipError_t launch_quantize_rows_1x128(const uint16_t* x, const int32_t* src_row, int num_src, int rows, int cols,
+                                      uint8_t* out, float* scale_out, bool mn_major, hipStream_t stream);
 hipError_t launch_quantize_1x128(const uint16_t* x, int rows, int cols, uint8_t* out, float* scale_out,
                                  bool mn_major, hipStream_t stream);
 hipError_t launch_fused_add_rmsnorm_quant(const uint16_t* input, uint16_t* residual, const uint16_t* weight,

@@ -126,29 +126,6 @@ moe_permutation_kernel(const int32_t* __restrict__ ids, int entries, int top_k, 
 constexpr int kRowThreads = 256;  // 16 teams of 16 lanes, one 128-wide block per team and pass
 
 __global__ void __launch_bounds__(kRowThreads)
-moe_gather_quant_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ src_token,
-                        int num_tokens, int hidden, uint8_t* __restrict__ a_out,
-                        float* __restrict__ a_scale_out) {
-  const int row = blockIdx.x;
-  const int t = src_token != nullptr ? src_token[row] : row;  // null: rows are the tokens themselves
-  if (t < 0 || t >= num_tokens) return;
-  const int nblk = hidden / 128;
-  const int sub = threadIdx.x & 15;
-  const uint16_t* xrow = x + (int64_t)t * hidden;
-  uint8_t* orow = a_out + (int64_t)row * hidden;
-  for (int blk = threadIdx.x >> 4; blk < nblk; blk += kRowThreads / 16) {
-    const int col = blk * 128 + sub * 8;
-    float v[8];
-    unpack_bf16x8(*reinterpret_cast<const uint4*>(xrow + col), v);
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    amax = team16_max(amax);
-    quant_store_8(v, amax, orow + col, a_scale_out + (int64_t)row * nblk + blk, sub == 0);
-  }
-}
-
-__global__ void __launch_bounds__(kRowThreads)
 moe_silu_mul_quant_kernel(const uint16_t* __restrict__ y, const int32_t* __restrict__ m_indices,
                           int inter, uint8_t* __restrict__ a_out, float* __restrict__ a_scale_out) {
   const int row = blockIdx.x;
@@ -173,23 +150,37 @@ moe_silu_mul_quant_kernel(const uint16_t* __restrict__ y, const int32_t* __restr
   }
 }
 
-__global__ void __launch_bounds__(kRowThreads)
+// One workgroup per token with one lane per 8 columns (up to 1024 lanes; wider rows loop). A lane
+// loads its 8 columns of up to 8 routed rows before the first FMA, then sums in slot order.
+constexpr int kCombineBatch = 8;
+
+__global__ void __launch_bounds__(1024)
 moe_combine_kernel(const uint16_t* __restrict__ y, const int32_t* __restrict__ row_of_entry,
                    const float* __restrict__ weights, int top_k, int hidden, int m_alloc,
                    uint16_t* __restrict__ out) {
   const int t = blockIdx.x;
   const int32_t* rows = row_of_entry + (int64_t)t * top_k;
   const float* w = weights + (int64_t)t * top_k;
-  for (int c = threadIdx.x * 8; c < hidden; c += kRowThreads * 8) {
+  for (int c = threadIdx.x * 8; c < hidden; c += blockDim.x * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < top_k; ++s) {
-      const int r = rows[s];
-      if (r < 0 || r >= m_alloc) continue;
-      const float ws = w[s];
-      float v[8];
-      unpack_bf16x8(*reinterpret_cast<const uint4*>(y + (int64_t)r * hidden + c), v);
+    for (int s0 = 0; s0 < top_k; s0 += kCombineBatch) {
+      uint4 raw[kCombineBatch];
+      bool live[kCombineBatch];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(ws, v[i], acc[i]);
+      for (int j = 0; j < kCombineBatch; ++j) {
+        const int r = s0 + j < top_k ? rows[s0 + j] : -1;
+        live[j] = r >= 0 && r < m_alloc;
+        if (live[j]) raw[j] = *reinterpret_cast<const uint4*>(y + (int64_t)r * hidden + c);
+      }
+#pragma unroll
+      for (int j = 0; j < kCombineBatch; ++j) {
+        if (!live[j]) continue;
+        const float ws = w[s0 + j];
+        float v[8];
+        unpack_bf16x8(raw[j], v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(ws, v[i], acc[i]);
+      }
     }
     uint4 o;
     o.x = pack_bf16x2(acc[0], acc[1]);
@@ -217,9 +208,7 @@ hipError_t launch_moe_build_permutation(const int32_t* topk_ids, int num_tokens,
 hipError_t launch_moe_gather_quant(const uint16_t* x, const int32_t* src_token, int num_tokens,
                                    int hidden, int m_alloc, uint8_t* a_out, float* a_scale_out,
                                    hipStream_t stream) {
-  hipLaunchKernelGGL(moe_gather_quant_kernel, dim3(m_alloc), dim3(kRowThreads), 0, stream, x, src_token,
-                     num_tokens, hidden, a_out, a_scale_out);
-  return hipGetLastError();
+  return launch_quantize_rows_1x128(x, src_token, num_tokens, m_alloc, hidden, a_out, a_scale_out, false, stream);
 }
 
 hipError_t launch_moe_silu_mul_quant(const uint16_t* y, const int32_t* m_indices, int rows,
@@ -233,7 +222,8 @@ hipError_t launch_moe_silu_mul_quant(const uint16_t* y, const int32_t* m_indices
 hipError_t launch_moe_combine(const uint16_t* y, const int32_t* row_of_entry,
                               const float* topk_weights, int num_tokens, int top_k, int hidden,
                               int m_alloc, uint16_t* out, hipStream_t stream) {
-  hipLaunchKernelGGL(moe_combine_kernel, dim3(num_tokens), dim3(kRowThreads), 0, stream, y, row_of_entry,
+  const int threads = std::min(1024, (hidden / 8 + 63) / 64 * 64);
+  hipLaunchKernelGGL(moe_combine_kernel, dim3(num_tokens), dim3(threads), 0, stream, y, row_of_entry,
                      topk_weights, top_k, hidden, m_alloc, out);
   return hipGetLastError();
 }

@@ -60,11 +60,12 @@ def _require_cuda(a: torch.Tensor) -> torch.device:
 
 
 def fp8_gemm_nt_groupwise(a, b, a_scale, b_scale, out, scale_major="K", granularity=_GRAN) -> torch.Tensor:
-    """out (m,n) bf16 or fp16 = a (m,k) @ b (n,k).T with 1x128 / 128x128 FP32 scales."""
+    """out (m,n) bf16 or fp16 = a (m,k) @ b (n,k).T with 1x128 / 128x128 FP32 scales (any n: b_scale
+    has ceil(n/128) blocks)."""
     dev = _require_cuda(a)
     m, k = a.shape
     n = b.shape[0]
-    kb, nb = k // 128, n // 128
+    kb, nb = k // 128, (n + 127) // 128
     major = _major(scale_major)
     _check(a, "a", _FP8_DTYPES, (m, k), dev)
     _check(b, "b", _FP8_DTYPES, (n, k), dev)
@@ -75,6 +76,30 @@ def fp8_gemm_nt_groupwise(a, b, a_scale, b_scale, out, scale_major="K", granular
         st = _lib.load().fp8_gemm_nt_groupwise(_ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale), _ptr(out),
                                                _out_code(out), m, n, k, major, *granularity, _stream(dev))
     _lib.check(st, "fp8_gemm_nt_groupwise")
+    return out
+
+
+def fp8_gemm_nt_groupwise_fp8_out(a, b, a_scale, b_scale, output_scale, out, scale_major="K",
+                                  granularity=_GRAN) -> torch.Tensor:
+    """out (m,n) E4M3 codes = E4M3(saturate(a @ b.T / output_scale[0])), output_scale a 1-element FP32
+    device tensor (the per-tensor dequantisation scale of the output)."""
+    dev = _require_cuda(a)
+    m, k = a.shape
+    n = b.shape[0]
+    kb, nb = k // 128, (n + 127) // 128
+    major = _major(scale_major)
+    _check(a, "a", _FP8_DTYPES, (m, k), dev)
+    _check(b, "b", _FP8_DTYPES, (n, k), dev)
+    _check(a_scale, "a_scale", (torch.float32,), (m, kb) if major == 0 else (kb, m), dev)
+    _check(b_scale, "b_scale", (torch.float32,), (nb, kb) if major == 0 else (kb, nb), dev)
+    _check(output_scale, "output_scale", (torch.float32,), tuple(output_scale.shape), dev)
+    if output_scale.numel() != 1:
+        raise ValueError(f"output_scale must hold one element (per-tensor scale), got shape {tuple(output_scale.shape)}")
+    _check(out, "out", _FP8_DTYPES, (m, n), dev)
+    with torch.cuda.device(dev):
+        st = _lib.load().fp8_gemm_nt_groupwise_fp8_out(_ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale), _ptr(out),
+                                                       _ptr(output_scale), m, n, k, major, *granularity, _stream(dev))
+    _lib.check(st, "fp8_gemm_nt_groupwise_fp8_out")
     return out
 
 
@@ -163,19 +188,27 @@ def gemm_fp8_nt_groupwise(a: torch.Tensor, b: torch.Tensor, a_scale: torch.Tenso
                           out_dtype: Optional[torch.dtype] = None, backend: str = "auto",
                           output_scale: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Groupwise FP8 NT GEMM with the MATE page's parameters; ``mma_sm`` has no meaning here and is
-    ignored, ``backend`` must be 'auto', FP8 output (``output_scale``) is not implemented. A 0-d
-    ``b_scale`` is one scale for every 128x128 block of b."""
+    ignored, ``backend`` must be 'auto'. With ``output_scale`` (a one-element FP32 tensor) the output
+    is E4M3 (``out_dtype`` torch.float8_e4m3fn, the default then, or torch.uint8). A 0-d ``b_scale``
+    is one scale for every 128x128 block of b."""
     if backend != "auto":
         raise NotImplementedError("backend must be 'auto'")
-    if output_scale is not None:
-        raise NotImplementedError("FP8 output (output_scale) is not implemented")
-    dtype = _out_dtype(out, out_dtype)
     m, k = a.shape
     n = b.shape[0]
     major = _major(scale_major_mode)
     if b_scale.dim() == 0:
-        shape = (n // 128, k // 128) if major == 0 else (k // 128, n // 128)
+        nb = (n + 127) // 128
+        shape = (nb, k // 128) if major == 0 else (k // 128, nb)
         b_scale = b_scale.to(torch.float32).expand(shape).contiguous()
+    if output_scale is not None:
+        if out is None:
+            dtype = torch.float8_e4m3fn if out_dtype is None else out_dtype
+            if dtype not in _FP8_DTYPES:
+                raise NotImplementedError("with output_scale the output is E4M3 (torch.float8_e4m3fn or uint8)")
+            out = torch.empty((m, n), dtype=dtype, device=a.device)
+        return fp8_gemm_nt_groupwise_fp8_out(a, b, a_scale, b_scale, output_scale, out, major,
+                                             tuple(scale_granularity_mnk))
+    dtype = _out_dtype(out, out_dtype)
     if out is None:
         out = torch.empty((m, n), dtype=dtype, device=a.device)
     return fp8_gemm_nt_groupwise(a, b, a_scale, b_scale, out, major, tuple(scale_granularity_mnk))

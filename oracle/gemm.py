@@ -26,7 +26,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .e4m3 import decode
+from .e4m3 import MAX_FINITE as MAX_E4M3, decode, encode_rne
 
 BLOCK = 128
 
@@ -56,17 +56,28 @@ def gemm_fp8_nt_groupwise(a, b, a_scale, b_scale, scale_major: str = "K") -> np.
     b = np.asarray(b)
     m, k = a.shape
     n, kb_ = b.shape
-    if kb_ != k or k % BLOCK or n % BLOCK:
-        raise ValueError("need a (m,k), b (n,k), k and n multiples of 128")
-    k_blocks, n_blocks = k // BLOCK, n // BLOCK
+    if kb_ != k or k % BLOCK:
+        raise ValueError("need a (m,k), b (n,k), k a multiple of 128")
+    # any n: column j uses b-scale block j // 128, so there are ceil(n/128) blocks
+    k_blocks, n_blocks = k // BLOCK, -(-n // BLOCK)
     sa, sb = _scales_k_major(a_scale, b_scale, m, n_blocks, k_blocks, scale_major)
     ref = np.zeros((m, n), dtype=np.float64)
     for kb in range(k_blocks):
         ks = slice(kb * BLOCK, (kb + 1) * BLOCK)
         block = decode(a[:, ks]) @ decode(b[:, ks]).T          # exact block sums
-        scale = sa[:, kb][:, None] * np.repeat(sb[:, kb], BLOCK)[None, :]
+        scale = sa[:, kb][:, None] * np.repeat(sb[:, kb], BLOCK)[None, :n]
         ref += block * scale
     return ref
+
+
+def fp8_output_codes(values, output_scale) -> np.ndarray:
+    """E4M3 codes of the FP8-output variant (``output_scale`` of gemm_fp8_nt_groupwise): the value
+    divided by the per-tensor scale in float32 (the precision the GPU decides the code in),
+    saturated to +-448, rounded to nearest even; NaN stays NaN."""
+    v32 = np.asarray(values, dtype=np.float64).astype(np.float32)
+    q = v32 / np.float32(output_scale)
+    q = np.where(np.isnan(q), q, np.clip(q, -MAX_E4M3, MAX_E4M3)).astype(np.float32)
+    return encode_rne(q)
 
 
 def group_gemm_contiguous(a, b, a_scale, b_scale, m_indices, rows=None) -> np.ndarray:

@@ -60,9 +60,20 @@ def test_plain_rejects_k_not_multiple_of_128(lib):
     assert st == _lib.INVALID_ARGUMENT and "k (100)" in msg
 
 
-def test_plain_rejects_n_not_multiple_of_128(lib):
+def test_n_tails_only_in_the_plain_form(lib):
+    # the plain form takes any n (validation passes; without a GPU the call stops at the device check)
     st, msg = _status(lib.fp8_gemm_nt_groupwise, P, P, P, P, P, 0, 4, 200, 128, 0, *GRAN, None)
+    assert "n (200)" not in msg and st != _lib.OK
+    st, msg = _status(lib.fp8_group_gemm_contiguous, P, P, P, P, P, P, 0, 128, 200, 128, 2, 0, *GRAN, None)
     assert st == _lib.INVALID_ARGUMENT and "n (200)" in msg
+    st, msg = _status(lib.fp8_batch_gemm_masked, P, P, P, P, P, 1, P, 0, 2, 64, 200, 128, 0, *GRAN, None)
+    assert st == _lib.INVALID_ARGUMENT and "n (200)" in msg
+
+
+def test_fp8_output_needs_a_scale(lib):
+    st, msg = _status(lib.fp8_gemm_nt_groupwise_fp8_out, P, P, P, P, P, None, 4, 128, 128, 0, *GRAN, None)
+    assert st == _lib.INVALID_ARGUMENT and "output_scale" in msg
+    assert lib.fp8_gemm_nt_groupwise_fp8_out(None, None, None, None, None, P, 0, 128, 128, 0, *GRAN, None) == _lib.OK
 
 
 def test_plain_rejects_negative_sizes_and_bad_layout(lib):

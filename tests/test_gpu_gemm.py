@@ -13,7 +13,7 @@ import torch
 
 import moe_expert_matmul_amd as fp8g
 import workloads
-from oracle import bf16, gemm as ogemm
+from oracle import bf16, e4m3, gemm as ogemm
 from parity import assert_within_tolerance, bf16_values, fp16_values, host, say, sentinel_like, untouched
 
 pytestmark = pytest.mark.gpu
@@ -48,6 +48,86 @@ def test_plain_matches_oracle(m, n, k):
     d = workloads.plain(m, n, k, seed=m + n + k, device=DEV)
     out = _plain_call(d)
     assert_within_tolerance(bf16_values(out), _plain_ref(d), f"plain {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(37, 100, 256), (300, 200, 512), (129, 130, 384), (513, 4100, 256), (1, 1, 128)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_plain_n_tails_match_oracle(m, n, k, dtype):
+    """Any n in the plain form: the last b-scale block covers n % 128 rows; n % 4 != 0 takes the
+    element-wise stores. Every element of out is written, in both scale layouts and every tile."""
+    say("plain n tail", m, n, k, dtype)
+    d = workloads.plain(m, n, k, seed=m + n, device=DEV)
+    ref = _plain_ref(d)
+    values = bf16_values if dtype == torch.bfloat16 else fp16_values
+    outs = []
+    try:
+        for tile in ("256x256", "128x256", "256x128", "128x128"):
+            os.environ["FP8G_TILE"] = tile
+            for major in ("K", "MN"):
+                out = _plain_call(d, major, out=sentinel_like((m, n), DEV, dtype))
+                assert not untouched(out).any(), f"unwritten outputs ({tile}, {major})"
+                outs.append(host(out))
+    finally:
+        os.environ.pop("FP8G_TILE", None)
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+    assert_within_tolerance(values(torch.from_numpy(outs[0].view(np.int16)).view(dtype)), ref, f"n tail {m}x{n}x{k}")
+
+
+def _midpoint_distance(q):
+    """Relative distance of float32 quotients to the nearest rounding midpoint between E4M3 codes."""
+    table = np.sort(np.unique(np.abs(e4m3.decode(np.arange(256, dtype=np.uint8)))))
+    table = table[np.isfinite(table)]
+    mids = (table[1:] + table[:-1]) / 2
+    aq = np.abs(q.astype(np.float64))
+    idx = np.clip(np.searchsorted(mids, aq), 1, len(mids) - 1)
+    near = np.minimum(np.abs(aq - mids[idx]), np.abs(aq - mids[idx - 1]))
+    return near / np.maximum(aq, 1e-30)
+
+
+@pytest.mark.parametrize("m,n,k,s", [(300, 384, 512, 0.37), (129, 200, 1024, 1.3), (64, 130, 256, 0.011)])
+def test_fp8_output_bit_exact_on_exact_products(m, n, k, s):
+    """output_scale (E4M3 output): out = E4M3(saturate(acc / s)). With integer codes in [-4, 4] and
+    power-of-two scales every partial sum is exact in FP32, so the GPU's accumulator equals the exact
+    value and every code -- saturated ones included -- must equal the oracle's."""
+    say("fp8 output exact", m, n, k, s)
+    rng = np.random.default_rng(m + n)
+    ints = lambda shape: torch.from_numpy(rng.integers(-4, 5, shape).astype(np.float32))
+    a = ints((m, k)).to(torch.float8_e4m3fn).view(torch.uint8).to(DEV)
+    b = ints((n, k)).to(torch.float8_e4m3fn).view(torch.uint8).to(DEV)
+    nb = -(-n // 128)
+    sa = torch.from_numpy(np.exp2(rng.integers(-3, 4, (m, k // 128))).astype(np.float32)).to(DEV)
+    sb = torch.from_numpy(np.exp2(rng.integers(-3, 4, (nb, k // 128))).astype(np.float32)).to(DEV)
+    osc = torch.tensor([s], dtype=torch.float32, device=DEV)
+    out = fp8g.gemm_fp8_nt_groupwise(a, b, sa, sb, output_scale=osc)
+    torch.cuda.synchronize()
+    assert out.dtype == torch.float8_e4m3fn
+    ref = ogemm.gemm_fp8_nt_groupwise(host(a), host(b), host(sa), host(sb))
+    want = ogemm.fp8_output_codes(ref, np.float32(s))
+    assert np.array_equal(host(out.view(torch.uint8)), want)
+    assert (np.abs(e4m3.decode(want)) == 448).any() and (np.abs(e4m3.decode(want)) < 448).any()
+
+
+@pytest.mark.parametrize("m,n,k", [(300, 384, 512), (129, 200, 1024)])
+def test_fp8_output_within_tolerance(m, n, k):
+    """Random workload: the GPU decides each code from its FP32 accumulator, which may differ from
+    the exact value by the GEMM tolerance (8e-3|ref| + 1e-3 rms). Its code must be one of the codes
+    the oracle gives anywhere in that band around the exact value."""
+    say("fp8 output tolerance", m, n, k)
+    d = workloads.plain(m, n, k, seed=m * 3 + n, device=DEV)
+    ref = _plain_ref(d)
+    s = np.float32(np.abs(ref).max() / 600.0)  # the largest outputs saturate
+    osc = torch.tensor([s], dtype=torch.float32, device=DEV)
+    out = torch.empty((m, n), dtype=torch.uint8, device=DEV)
+    fp8g.fp8_gemm_nt_groupwise_fp8_out(d["a"], d["b"], d["a_scale"], d["b_scale"], osc, out)
+    torch.cuda.synchronize()
+    gc = host(out)
+    band = 8e-3 * np.abs(ref) + 1e-3 * np.sqrt(np.mean(ref ** 2))
+    lo, hi = ogemm.fp8_output_codes(ref - band, s), ogemm.fp8_output_codes(ref + band, s)
+    g = e4m3.decode(gc)
+    assert np.all((g >= e4m3.decode(lo)) & (g <= e4m3.decode(hi))), "code outside the tolerance band"
+    exact = ogemm.fp8_output_codes(ref, s)
+    assert np.mean(gc != exact) < 1e-2
+    assert (np.abs(g) == 448).any()
 
 
 @pytest.mark.parametrize("m,n,k", [(300, 640, 1024), (4096, 512, 256)])

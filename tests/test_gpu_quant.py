@@ -22,6 +22,8 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 CASES = [(1, 128), (3, 384), (67, 1152), (130, 7168), (4096, 7168)]
+# hidden beyond 64 blocks: two and four blocks per team in registers, and the re-reading kernel
+WIDE = [(5, 12800), (3, 25600), (2, 38400)]
 
 
 def _scales_k_major(scales: np.ndarray, major: str) -> np.ndarray:
@@ -29,7 +31,7 @@ def _scales_k_major(scales: np.ndarray, major: str) -> np.ndarray:
 
 
 @pytest.mark.parametrize("major", ["K", "MN"])
-@pytest.mark.parametrize("rows,cols", CASES[:4] + [(0, 256)])
+@pytest.mark.parametrize("rows,cols", CASES[:4] + [(7, 2304), (0, 256), (2, 38400)])
 def test_quantize_1x128_bit_exact(rows, cols, major):
     say("quantize_1x128", rows, cols, major)
     g = torch.Generator(device=DEV).manual_seed(rows * 7 + cols)
@@ -75,7 +77,7 @@ def _norm_inputs(rows, hidden, seed):
 
 
 @pytest.mark.parametrize("major", ["K", "MN"])
-@pytest.mark.parametrize("rows,hidden", CASES)
+@pytest.mark.parametrize("rows,hidden", CASES + WIDE)
 def test_fused_add_rmsnorm_quant_matches_oracle(rows, hidden, major):
     say("fused_add_rmsnorm_quant", rows, hidden, major)
     d = _norm_inputs(rows, hidden, seed=rows + hidden)

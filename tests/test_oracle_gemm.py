@@ -175,7 +175,53 @@ def test_plain_equals_single_group_masked_and_contiguous():
     assert np.array_equal(plain, masked) and np.array_equal(plain, contig)
 
 
-def test_rejects_k_or_n_not_multiple_of_128():
+def test_rejects_k_not_multiple_of_128():
     with pytest.raises(ValueError):
         gemm.gemm_fp8_nt_groupwise(np.zeros((2, 100), np.uint8), np.zeros((128, 100), np.uint8),
                                    np.ones((2, 1), np.float32), np.ones((1, 1), np.float32))
+
+
+@pytest.mark.parametrize("n", [1, 100, 130, 200])
+def test_n_tail_is_the_leading_columns_of_a_padded_b(n):
+    # Column j uses b-scale block j // 128 whatever n is: the result for n columns equals the first n
+    # columns of the product with b padded by arbitrary rows to whole 128-row blocks.
+    rng = np.random.default_rng(n)
+    m, k = 6, 256
+    nb = -(-n // 128)
+    a, b_full = _random_codes(rng, (m, k)), _random_codes(rng, (nb * 128, k))
+    sa, sb = _random_scales(rng, (m, 2)), _random_scales(rng, (nb, 2))
+    full = gemm.gemm_fp8_nt_groupwise(a, b_full, sa, sb)
+    assert np.array_equal(gemm.gemm_fp8_nt_groupwise(a, b_full[:n], sa, sb), full[:, :n])
+    assert np.array_equal(gemm.gemm_fp8_nt_groupwise(a, b_full[:n], sa.T.copy(), sb.T.copy(), "MN"), full[:, :n])
+
+
+def test_n_tail_brute_force():
+    rng = np.random.default_rng(9)
+    a, b = _random_codes(rng, (2, 128)), _random_codes(rng, (3, 128))
+    sa, sb = _random_scales(rng, (2, 1)), _random_scales(rng, (1, 1))
+    av, bv = _torch_values(a), _torch_values(b)
+    ref = gemm.gemm_fp8_nt_groupwise(a, b, sa, sb)
+    for i in range(2):
+        for j in range(3):
+            exact = sum(Fraction(av[i, t]) * Fraction(bv[j, t]) for t in range(128))
+            exact *= Fraction(float(sa[i, 0])) * Fraction(float(sb[0, 0]))
+            assert Fraction(ref[i, j]) == exact or abs(Fraction(ref[i, j]) - exact) <= abs(exact) * Fraction(1, 2 ** 52)
+
+
+def test_fp8_output_codes_closed_forms():
+    # E4M3: 1.0 = 0x38, 1.125 = 0x39, 1.25 = 0x3A, 256 = 0x78, 448 = 0x7E; NaN = 0x7F.
+    vals = np.array([2.0, 2.125, 2.375, 512.0, 896.0, 1000.0, -1e30, np.inf, np.nan, 0.0, -2.0])
+    codes = gemm.fp8_output_codes(vals, 2.0)
+    # 2.125/2 = 1.0625 is the midpoint of 1 and 1.125 -> even 0x38; 2.375/2 = 1.1875 -> even 0x3A;
+    # beyond 448 saturates; NaN stays NaN
+    assert codes.tolist() == [0x38, 0x38, 0x3A, 0x78, 0x7E, 0x7E, 0xFE, 0x7E, 0x7F, 0x00, 0xB8]
+
+
+def test_fp8_output_of_an_all_ones_product():
+    # a = b = 1, k = 128, unit scales: every output is 128; with output scale 0.5 the code is 256
+    # (0x78), with 0.25 the quotient 512 saturates to 448 (0x7E), with 1024 it is 0.125 (0x20).
+    a = np.full((4, 128), ONE, np.uint8)
+    vals = gemm.gemm_fp8_nt_groupwise(a, a, np.ones((4, 1), np.float32), np.ones((1, 1), np.float32))
+    assert np.all(gemm.fp8_output_codes(vals, 0.5) == 0x78)
+    assert np.all(gemm.fp8_output_codes(vals, 0.25) == 0x7E)
+    assert np.all(gemm.fp8_output_codes(vals, 1024.0) == 0x20)

@@ -66,10 +66,15 @@ def _quantized_matrix(shape, block_rows, gen, device):
 
 
 def plain(m: int, n: int, k: int, seed: int = 0, device="cpu"):
-    """Plain form inputs: a (m,k), b (n,k) E4M3 codes; a_scale (m,k/128), b_scale (n/128,k/128)."""
+    """Plain form inputs: a (m,k), b (n,k) E4M3 codes; a_scale (m,k/128), b_scale (ceil(n/128),k/128).
+    When n is not a multiple of 128, b is drawn and quantised with whole 128-row blocks and cut to
+    its first n rows (the last block's scale then covers its n % 128 remaining rows)."""
     g = _gen(seed, device)
     a, sa = _quantized_matrix((m, k), 1, g, device)
-    b, sb = _quantized_matrix((n, k), BLOCK, g, device)
+    n_pad = -(-n // BLOCK) * BLOCK
+    b, sb = _quantized_matrix((n_pad, k), BLOCK, g, device)
+    if n_pad != n:
+        b = b[:n].contiguous()
     return dict(a=a, b=b, a_scale=sa, b_scale=sb, m=m, n=n, k=k)
 
 
