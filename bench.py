@@ -11,7 +11,8 @@ kernel source, else null. ``cpu_baseline`` times the float64 CPU oracle on a bou
 the same workload.
 
 --configs adds the other workloads (contiguous grouped over 32 Zipf-sized experts, masked batched
-over 16 groups, the add-RMSNorm + 1x128 quantiser and the plain quantiser over 4096x7168 BF16, the
+over 16 groups, the channelwise-scaled batched GEMM (8 x 1024x4096x7168, B transposed in the
+call), the add-RMSNorm + 1x128 quantiser and the plain quantiser over 4096x7168 BF16, the
 4096-token expert FFN), each timed per launch with the caches evicted in between by a 512 MB read,
 under "configs".
 """
@@ -156,6 +157,18 @@ def other_configs(steps, warmup):
         "hbm_gbs": round(hbm / med / 1e6, 1), "frac_hbm": round(hbm / med / 1e6 / HBM_PEAK_GBS, 4),
         "frac_mfma": round(flops / med / 1e9 / FP8_DENSE_PEAK_TFLOPS, 4), "sum_masked_m": int(mm.sum())}
     del d, out
+
+    d = workloads.bmm(8, 1024, 4096, 7168, True, True, seed=0, device=dev)
+    out = torch.empty((8, 1024, 4096), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(8 * 4096 * 7168, dtype=torch.uint8, device=dev)
+    sa, sb = d["a_scale"].reshape(8, 1024), d["b_scale"].reshape(8, 4096)
+    fn = lambda: fp8g.fp8_bmm(d["a"], d["b"], sa, sb, out, ws, True, True)
+    med, best = time_cold(fn, steps, warmup, flush)
+    flops = 2.0 * 8 * 1024 * 4096 * 7168
+    res["bmm_channelwise_8x1024x4096x7168"] = {
+        "ms": round(med, 4), "ms_best": round(best, 4), "tflops": round(flops / med / 1e9, 2),
+        "frac_mfma": round(flops / med / 1e9 / FP8_DENSE_PEAK_TFLOPS, 4)}
+    del d, out, ws
 
     d = workloads.norm(4096, 7168, seed=0, device=dev)
     res_t = d["residual"].clone()

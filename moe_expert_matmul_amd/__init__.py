@@ -8,6 +8,8 @@ touch the GPU; the first call loads the library and fails loudly if it has not b
 from ._lib import Fp8gError, Fp8gInvalidArgument, Fp8gNotSupported, LIB_PATH, load  # noqa: F401
 from .gemm import (  # noqa: F401
     batch_deepgemm_fp8_nt_groupwise,
+    bmm_fp8,
+    fp8_bmm,
     fp8_batch_gemm_masked,
     fp8_gemm_nt_groupwise,
     fp8_gemm_nt_groupwise_fp8_out,

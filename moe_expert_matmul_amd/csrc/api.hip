@@ -447,6 +447,65 @@ fp8g_status_t fp8_moe_gather_quant(const void* x, const int32_t* src_token, int6
   });
 }
 
+int64_t fp8_bmm_workspace_size(int64_t batch, int64_t n, int64_t k) {
+  if (batch < 0 || n < 0 || k < 0) return -1;
+  return batch * n * k;
+}
+
+fp8g_status_t fp8_bmm(const void* a, const void* b, const float* a_scale, int32_t a_scale_per_row,
+                      const float* b_scale, int32_t b_scale_per_col, void* out, int32_t out_dtype, int64_t batch,
+                      int64_t m, int64_t n, int64_t k, void* workspace, int64_t workspace_bytes, void* stream) {
+  return guarded([&] {
+    require(batch >= 0 && batch <= 65535, "batch (%lld) must be in [0, 65535]", (long long)batch);
+    check_gemm_dims(m, n, k, /*n_tail=*/true);
+    require(n % 16 == 0, "n (%lld) must be a multiple of 16", (long long)n);
+    check_out_dtype(out_dtype);
+    require(a_scale_per_row == 0 || a_scale_per_row == 1, "a_scale_per_row must be 0 or 1");
+    require(b_scale_per_col == 0 || b_scale_per_col == 1, "b_scale_per_col must be 0 or 1");
+    if (batch == 0 || m == 0 || n == 0) return;
+    require(batch * m * n <= ((int64_t)1 << 40) && batch * n * k <= ((int64_t)1 << 40), "sizes too large");
+    require(out && a_scale && b_scale, "out and the scales must be non-null");
+    require(k == 0 || (a && b && workspace), "a, b and the workspace must be non-null");
+    require(workspace_bytes >= batch * n * k, "workspace (%lld bytes) must hold batch*n*k = %lld bytes",
+            (long long)workspace_bytes, (long long)(batch * n * k));
+    require(aligned(a, 16) && aligned(b, 16) && aligned(out, 16) && aligned(workspace, 16),
+            "a, b, out and the workspace must be 16-byte aligned");
+    require(aligned(a_scale, 4) && aligned(b_scale, 4), "scales must be 4-byte aligned");
+    check_device();
+    if (k > 0)
+      check_hip(fp8g::launch_transpose_bytes(static_cast<const uint8_t*>(b), (int)batch, (int)k, (int)n,
+                                             static_cast<uint8_t*>(workspace), (hipStream_t)stream),
+                "fp8_bmm transpose launch");
+    fp8g::GemmParams p{};
+    p.a = static_cast<const uint8_t*>(a);
+    p.b = static_cast<const uint8_t*>(workspace);
+    p.sa = a_scale;
+    p.sb = b_scale;
+    p.out = static_cast<uint16_t*>(out);
+    p.out_fp16 = out_dtype == FP8G_OUT_FP16;
+    p.bmm_sa_rows = a_scale_per_row;
+    p.bmm_sb_cols = b_scale_per_col;
+    p.m = (int32_t)m;
+    p.n = (int32_t)n;
+    p.k = (int32_t)k;
+    p.kblocks = (int32_t)(k / 128);
+    p.nblocks = (int32_t)ceil_div(n, 128);
+    p.num_groups = (int32_t)batch;
+    p.a_src_rows = (int32_t)m;
+    p.a_group_stride = m * k;
+    p.b_group_stride = n * k;
+    p.out_group_stride = m * n;
+    fp8g::TileConfig cfg = m > 128 ? fp8g::TILE_256x256 : fp8g::TILE_128x256;
+    if (fp8g::tile_override() >= 0) cfg = (fp8g::TileConfig)fp8g::tile_override();
+    p.tiles_m = (int32_t)ceil_div(m, fp8g::tile_rows(cfg));
+    p.tiles_n = (int32_t)ceil_div(n, fp8g::tile_cols(cfg));
+    p.group_m = 4;
+    const int64_t grid = batch * p.tiles_m * p.tiles_n;
+    require(grid <= kInt32Max, "too many tiles");
+    check_hip(fp8g::launch_gemm(fp8g::MODE_BMM, cfg, p, (int)grid, (hipStream_t)stream), "fp8_bmm launch");
+  });
+}
+
 fp8g_status_t fp8_quantize_1x128(const void* x, int64_t rows, int64_t cols, void* out, float* scale_out,
                                  int32_t scale_major, void* stream) {
   return guarded([&] {

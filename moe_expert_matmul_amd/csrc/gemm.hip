@@ -154,7 +154,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   // ---- tile scheduling ---------------------------------------------------------------------
   int t = xcd_local_order(blockIdx.x, gridDim.x);
   int g = 0;
-  if (MODE == MODE_MASKED) {
+  if (MODE == MODE_MASKED || MODE == MODE_BMM) {
     const int per = p.tiles_m * p.tiles_n;
     g = t / per;
     t -= g * per;
@@ -179,7 +179,9 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   // covers its own half (or exits when that half is padding only).
   int bsel = 0;
   int half_mask = 3;
-  if (MODE == MODE_MASKED) {
+  if (MODE == MODE_BMM) {
+    bsel = g;
+  } else if (MODE == MODE_MASKED) {
     const int mm = max(0, min(p.rowinfo[g], p.m));
     if (row0 >= mm) return;
     row_end = mm;
@@ -304,7 +306,9 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
       const int q = i - T::A_LOADS;
       load_lds_16(live ? rB : rNone, sA + T::A_BYTES + (wave * T::B_LOADS + q) * 1024, b_off[q], koff);
     } else {
-      load_lds_4(live ? rS : rNone, sA + s_dst, s_voff, (uint32_t)kb * s_kb_bytes);
+      // BMM: the scales act in the epilogue; the load still runs (through rNone) so that every
+      // mode issues the same loads per K block
+      load_lds_4(live && MODE != MODE_BMM ? rS : rNone, sA + s_dst, s_voff, (uint32_t)kb * s_kb_bytes);
     }
   };
   auto issue_loads = [&](int kb, bool live) {
@@ -318,6 +322,36 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   // the next block's loads, reads the b fragment of group jg+BPRE, and alternates one MFMA of
   // group jg with the four promotion FMAs of group jg-1, so the matrix core never waits on a VALU
   // read of its own result and no LDS read is hoisted far ahead of its use.
+  // BMM: the same issue order without scales -- each MFMA accumulates straight into acc, over all
+  // of K, and the scales are applied once in the epilogue.
+  auto compute_bmm = [&](int kb, int kb_load, bool load_live) {
+    const uint8_t* sA = smem + (kb % STAGES) * T::STAGE_BYTES;
+    const uint8_t* sB = sA + T::A_BYTES;
+    i32x8 af[T::IG];
+#pragma unroll
+    for (int ig = 0; ig < T::IG; ++ig) af[ig] = load_frag(sA, i0 + ig * 16 + fr, lane);
+    i32x8 bq[T::JG];
+#pragma unroll
+    for (int jg = 0; jg < BPRE && jg < T::JG; ++jg) bq[jg] = load_frag(sB, j0 + jg * 16 + fr, lane);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int jg = 0; jg < T::JG; ++jg) {
+#pragma unroll
+      for (int i = load_first(jg); i < load_first(jg + 1); ++i) issue_load(kb_load, i, load_live);
+      if (jg + BPRE < T::JG) bq[jg + BPRE] = load_frag(sB, j0 + (jg + BPRE) * 16 + fr, lane);
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int ig = 0; ig < T::IG; ++ig)
+        acc[ig][jg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bq[jg], af[ig], acc[ig][jg], FMT_E4M3, FMT_E4M3,
+                                                                      0, E8M0_ONE, 0, E8M0_ONE);
+      sched_vmem_group(load_first(jg + 1) - load_first(jg));
+      if (jg + BPRE < T::JG) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, T::IG, 0);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   auto compute = [&](int kb, int kb_load, bool load_live) {
     const uint8_t* sA = smem + (kb % STAGES) * T::STAGE_BYTES;
     const uint8_t* sB = sA + T::A_BYTES;
@@ -392,9 +426,12 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     wait_vmcnt<(STAGES - 2) * T::LOADS>();
     lds_pipeline_barrier();
     const int kb_load = kb + STAGES - 1;
-    if (wave_live)
-      compute(kb, kb_load, kb_load < KB);
-    else
+    if (wave_live) {
+      if constexpr (MODE == MODE_BMM)
+        compute_bmm(kb, kb_load, kb_load < KB);
+      else
+        compute(kb, kb_load, kb_load < KB);
+    } else
       issue_loads(kb_load, kb_load < KB);
   }
   wait_vmcnt<0>();  // the zero-fill loads of the last iterations
@@ -411,6 +448,24 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   if (wave_live) {
   const int jl = (lane >> 4) * 4;
   const bool vec = (p.n & 3) == 0;
+  if constexpr (MODE == MODE_BMM) {
+    // out = sa * sb * acc in FP32 (one rounding per product), before the output rounding
+    const float* SAg = p.sa + (p.bmm_sa_rows ? (int64_t)g * p.m : 0);
+    const float* SBg = p.sb + (p.bmm_sb_cols ? (int64_t)g * p.n : 0);
+#pragma unroll
+    for (int ig = 0; ig < T::IG; ++ig) {
+      const int i = min(row0 + i0 + ig * 16 + fr, p.m - 1);
+      const float sav = SAg[p.bmm_sa_rows ? i : 0];
+#pragma unroll
+      for (int jg = 0; jg < T::JG; ++jg) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = min(col0 + j0 + jg * 16 + jl + r, p.n - 1);
+          acc[ig][jg][r] = acc[ig][jg][r] * (sav * SBg[p.bmm_sb_cols ? j : 0]);
+        }
+      }
+    }
+  }
   if (MODE == MODE_PLAIN && p.out_scale != nullptr) {
     const float so = *p.out_scale;
     uint8_t* O = reinterpret_cast<uint8_t*>(p.out);
@@ -491,6 +546,9 @@ hipError_t launch_cfg(GemmMode mode, const GemmParams& p, int grid, hipStream_t 
       break;
     case MODE_MASKED:
       hipLaunchKernelGGL((gemm_fp8_groupwise_kernel<BM, BN, WM, WN, STAGES, MODE_MASKED>), dim3(grid), block, 0, stream, p);
+      break;
+    case MODE_BMM:
+      hipLaunchKernelGGL((gemm_fp8_groupwise_kernel<BM, BN, WM, WN, STAGES, MODE_BMM>), dim3(grid), block, 0, stream, p);
       break;
     case MODE_CONTIG_SWIGLU:
       if constexpr (BN == 256) {

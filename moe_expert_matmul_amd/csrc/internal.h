@@ -12,6 +12,7 @@ enum GemmMode : int {
   MODE_CONTIG = 1,  // per 128-row tile, b chosen by the tile's expert in m_indices
   MODE_MASKED = 2,  // per group g, rows below masked_m[g]
   MODE_CONTIG_SWIGLU = 3,  // contiguous, epilogue silu(gate) * up -> 1x128 E4M3 (expert-FFN fc1)
+  MODE_BMM = 4,     // per batch g: out = sa * sb * (a @ b.T), scales per tensor or per row / column
 };
 
 // Everything the GEMM kernel needs, passed by value as the kernel argument. Strides in elements.
@@ -30,6 +31,9 @@ struct GemmParams {
   int32_t out_fp16;
   // PLAIN only: E4M3 output, out[i][j] = E4M3_RNE(saturate(acc / out_scale[0])); null: 16-bit output
   const float* out_scale;
+  // BMM: a_scale holds one value (0) or one per row of each batch (1); b_scale one value or one per
+  // column of each batch; scale groups are m (a) and n (b) values apart.
+  int32_t bmm_sa_rows, bmm_sb_cols;
   int32_t inter;
   uint8_t* q_out;
   float* q_scale_out;
@@ -61,6 +65,8 @@ int tile_cols(TileConfig cfg);
 
 hipError_t launch_gemm(GemmMode mode, TileConfig cfg, GemmParams p, int grid, hipStream_t stream);
 
+hipError_t launch_transpose_bytes(const uint8_t* src, int batch, int rows, int cols, uint8_t* dst,
+                                  hipStream_t stream);
 hipError_t launch_quantize_rows_1x128(const uint16_t* x, const int32_t* src_row, int num_src, int rows, int cols,
                                       uint8_t* out, float* scale_out, bool mn_major, hipStream_t stream);
 hipError_t launch_quantize_1x128(const uint16_t* x, int rows, int cols, uint8_t* out, float* scale_out,

@@ -235,3 +235,61 @@ def batch_deepgemm_fp8_nt_groupwise(a: torch.Tensor, b: torch.Tensor, a_scale: t
         out = torch.empty((a.shape[0], a.shape[1], b.shape[1]), dtype=_out_dtype(None, out_dtype), device=a.device)
     return fp8_batch_gemm_masked(a, b, a_scale, b_scale, masked_m, expected_m, out, "K",
                                  tuple(scale_granularity_mnk))
+
+
+def fp8_bmm(a, b, a_scale, b_scale, out, workspace, a_scale_per_row: bool, b_scale_per_col: bool) -> torch.Tensor:
+    """out (batch,m,n) = sa * sb * (a (batch,m,k) @ b (batch,k,n)); a_scale is one value or (batch, m),
+    b_scale one value or (batch, n); workspace holds at least batch*n*k bytes."""
+    dev = _require_cuda(a)
+    batch, m, k = a.shape
+    n = b.shape[2]
+    _check(a, "a", _FP8_DTYPES, (batch, m, k), dev)
+    _check(b, "b", _FP8_DTYPES, (batch, k, n), dev)
+    _check(a_scale, "a_scale", (torch.float32,), (batch, m) if a_scale_per_row else tuple(a_scale.shape), dev)
+    _check(b_scale, "b_scale", (torch.float32,), (batch, n) if b_scale_per_col else tuple(b_scale.shape), dev)
+    if not a_scale_per_row and a_scale.numel() != 1:
+        raise ValueError("a per-tensor a_scale holds one value")
+    if not b_scale_per_col and b_scale.numel() != 1:
+        raise ValueError("a per-tensor b_scale holds one value")
+    _check(out, "out", _OUT_DTYPES, (batch, m, n), dev)
+    lib = _lib.load()
+    need = lib.fp8_bmm_workspace_size(batch, n, k)
+    if not (isinstance(workspace, torch.Tensor) and workspace.device == dev and workspace.is_contiguous()
+            and workspace.numel() * workspace.element_size() >= need):
+        raise ValueError(f"workspace must be a contiguous device tensor of at least {need} bytes")
+    with torch.cuda.device(dev):
+        st = lib.fp8_bmm(_ptr(a), _ptr(b), _ptr(a_scale), int(bool(a_scale_per_row)), _ptr(b_scale),
+                         int(bool(b_scale_per_col)), _ptr(out), _out_code(out), batch, m, n, k, _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), _stream(dev))
+    _lib.check(st, "fp8_bmm")
+    return out
+
+
+def _bmm_scale(scale: torch.Tensor, batch: int, size: int, channel_shape, name: str):
+    """(tensor, per_channel) from a tensorwise scalar or a rank-3 channelwise scale."""
+    if scale.numel() == 1:
+        return scale.reshape(1).to(torch.float32).contiguous(), False
+    if scale.dim() == 3 and tuple(scale.shape) == channel_shape:
+        return scale.reshape(batch, size).to(torch.float32).contiguous(), True
+    raise ValueError(f"{name} must be a scalar or have shape {channel_shape}, got {tuple(scale.shape)}")
+
+
+def bmm_fp8(A: torch.Tensor, B: torch.Tensor, A_scale: torch.Tensor, B_scale: torch.Tensor, dtype: torch.dtype,
+            out: Optional[torch.Tensor] = None, backend: str = "auto") -> torch.Tensor:
+    """Batched FP8 GEMM with the MATE page's parameters: A (batch,m,k), B (batch,k,n) E4M3; A_scale a
+    scalar or (batch, m, 1), B_scale a scalar or (batch, 1, n); BF16 or FP16 output. The K-major copy
+    of B is made in a workspace allocated here."""
+    if backend != "auto":
+        raise NotImplementedError("backend must be 'auto'")
+    if A.dtype == torch.float8_e5m2 or B.dtype == torch.float8_e5m2:
+        raise NotImplementedError("E5M2 inputs are not implemented (E4M3 only)")
+    batch, m, k = A.shape
+    n = B.shape[2]
+    sa, sa_rows = _bmm_scale(A_scale, batch, m, (batch, m, 1), "A_scale")
+    sb, sb_cols = _bmm_scale(B_scale, batch, n, (batch, 1, n), "B_scale")
+    if out is None:
+        if dtype not in _OUT_DTYPES:
+            raise NotImplementedError(f"dtype {dtype} is not implemented (BF16 or FP16)")
+        out = torch.empty((batch, m, n), dtype=dtype, device=A.device)
+    ws = torch.empty(max(1, batch * n * k), dtype=torch.uint8, device=A.device)
+    return fp8_bmm(A, B, sa, sb, out, ws, sa_rows, sb_cols)

@@ -21,7 +21,8 @@ Modules:
   bf16  -- round-to-nearest-even float -> bfloat16 encoder
   gemm  -- plain, contiguous-grouped and masked-batched groupwise GEMM references
   moe   -- the expert-FFN stages (1x128 quantiser, permutation, SiLU-mul, weighted combine)
+  bmm   -- batched FP8 GEMM with per-tensor or per-channel scales (bmm_fp8 of the MATE page)
   norm  -- fused add-RMSNorm with 1x128 FP8 quantisation (section "norm" of the MATE page)
 """
 
-from . import e4m3, bf16, gemm, moe, norm  # noqa: F401
+from . import e4m3, bf16, gemm, moe, norm, bmm  # noqa: F401

@@ -15,6 +15,8 @@ Workloads (all seed-fixed):
   moe          router logits ~ N(0,1) (T,E); p = softmax; top-k by p (ties -> lower expert index);
                weights = p at the chosen experts (not renormalised); X ~ N(0,1) in BF16;
                W1 (E, 2I, H) and W2 (E, H, I) ~ N(0,1) quantised per 128x128 block.
+  bmm          A (B,m,k), B (B,k,n) ~ N(0,1) quantised with amax/448 per row of A / per column of B
+               (channelwise) or per tensor.
   norm         add-RMSNorm input ~ N(0,1), residual ~ N(0,1) times a per-row log-uniform scale,
                weight ~ U(0.5, 1.5), all BF16.
 
@@ -143,6 +145,29 @@ def moe(num_tokens: int = 4096, hidden: int = 7168, num_experts: int = 64, top_k
     return dict(x=x, topk_ids=torch.from_numpy(ids).to(device), topk_weights=torch.from_numpy(w).to(device),
                 w1=w1, s1=s1, w2=w2, s2=s2, num_tokens=num_tokens, hidden=hidden,
                 num_experts=num_experts, top_k=top_k, inter=inter)
+
+
+def bmm(batch: int, m: int, n: int, k: int, channel_a: bool, channel_b: bool, seed: int = 0, device="cpu"):
+    """Batched FP8 GEMM inputs: A (batch,m,k), B (batch,k,n) ~ N(0,1) as E4M3 codes, with scale =
+    amax/448 per row of A / per column of B (channelwise, rank-3 scales (batch,m,1) / (batch,1,n)) or
+    over the whole tensor (tensorwise, 0-d scales)."""
+    g = _gen(seed, device)
+    x = _normal((batch, m, k), g, device)
+    y = _normal((batch, k, n), g, device)
+
+    def quant(t, dims):
+        amax = t.abs().amax(dim=dims, keepdim=True)
+        scale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+        codes = (t / scale).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+        return codes, scale.contiguous()
+
+    a, sa = quant(x, (2,) if channel_a else (0, 1, 2))
+    b, sb = quant(y, (1,) if channel_b else (0, 1, 2))
+    if not channel_a:
+        sa = sa.reshape(())
+    if not channel_b:
+        sb = sb.reshape(())
+    return dict(a=a, b=b, a_scale=sa, b_scale=sb, batch=batch, m=m, n=n, k=k)
 
 
 def norm(rows: int = 4096, hidden: int = 7168, seed: int = 0, device="cpu"):
