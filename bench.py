@@ -13,8 +13,10 @@ the same workload.
 --configs adds the other workloads (contiguous grouped over 32 Zipf-sized experts, masked batched
 over 16 groups, the channelwise-scaled batched GEMM (8 x 1024x4096x7168, B transposed in the
 call), the add-RMSNorm + 1x128 quantiser and the plain quantiser over 4096x7168 BF16, the
-4096-token expert FFN), each timed per launch with the caches evicted in between by a 512 MB read,
-under "configs".
+4096-token expert FFN with block scales and with per-tensor scales), each timed per launch with the caches evicted in between by a 512 MB read,
+under "configs". Two context lines are timed back to back like the headline: the per-tensor batched
+GEMM at batch 1 on the headline shape (the same matrix-core loop without per-block promotion), and
+hipBLASLt's per-tensor FP8 GEMM (torch._scaled_mm) on that shape, which is not this path.
 """
 
 from __future__ import annotations
@@ -170,6 +172,29 @@ def other_configs(steps, warmup):
         "frac_mfma": round(flops / med / 1e9 / FP8_DENSE_PEAK_TFLOPS, 4)}
     del d, out, ws
 
+    # The same matrix-core loop without per-block promotion (per-tensor scales, B transposed in the
+    # call) on the headline shape, and the vendor library's per-tensor FP8 GEMM (hipBLASLt through
+    # torch._scaled_mm) on the same shape, for context: both back to back, like the headline.
+    d = workloads.bmm(1, 4096, 4096, 7168, False, False, seed=0, device=dev)
+    out = torch.empty((1, 4096, 4096), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(4096 * 7168, dtype=torch.uint8, device=dev)
+    sa, sb = d["a_scale"].reshape(1), d["b_scale"].reshape(1)
+    ms, _ = time_back_to_back(lambda: fp8g.fp8_bmm(d["a"], d["b"], sa, sb, out, ws, False, False), 50, 10)
+    flops = 2.0 * 4096 * 4096 * 7168
+    res["bmm_tensorwise_1x4096x4096x7168"] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 2),
+                                              "frac_mfma": round(flops / ms / 1e9 / FP8_DENSE_PEAK_TFLOPS, 4)}
+    try:
+        a8 = d["a"][0].view(torch.float8_e4m3fn)
+        b8 = d["b"][0].t().contiguous().view(torch.float8_e4m3fn)  # (n, k), K-major
+        one = torch.tensor(1.0, device=dev)
+        ms, _ = time_back_to_back(lambda: torch._scaled_mm(a8, b8.t(), scale_a=one, scale_b=one,
+                                                           out_dtype=torch.bfloat16), 50, 10)
+        res["reference_hipblaslt_fp8_tensorwise_4096x4096x7168"] = {
+            "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 2), "note": "vendor library, not this path"}
+    except Exception as e:  # the reference is context only
+        res["reference_hipblaslt_fp8_tensorwise_4096x4096x7168"] = {"error": f"{type(e).__name__}: {e}"[:200]}
+    del d, out, ws
+
     d = workloads.norm(4096, 7168, seed=0, device=dev)
     res_t = d["residual"].clone()
     normed = torch.empty_like(d["input"])
@@ -199,6 +224,18 @@ def other_configs(steps, warmup):
     rows = 4096 * 8
     flops = 2.0 * rows * 4096 * 7168 + 2.0 * rows * 7168 * 2048
     res["moe_ffn_4096tok_h7168_e64_top8_i2048"] = {
+        "ms": round(med, 4), "ms_best": round(best, 4), "tflops": round(flops / med / 1e9, 2),
+        "frac_mfma": round(flops / med / 1e9 / FP8_DENSE_PEAK_TFLOPS, 4)}
+    del d, ws, out
+
+    d = workloads.moe_per_tensor(seed=0, device=dev)
+    ws = fp8g.MoePerTensorWorkspace.allocate(4096, 8, 64, 7168, 2048, dev)
+    out = torch.empty((4096, 7168), dtype=torch.bfloat16, device=dev)
+    fn = lambda: fp8g.moe_ffn_fp8_per_tensor(d["x"], d["topk_ids"], d["w1"], d["w2"], d["fc1_dequant"],
+                                             d["fc2_quant"], d["fc2_dequant"], d["fc1_input_dequant"], out=out,
+                                             workspace=ws)
+    med, best = time_cold(fn, steps, warmup, flush)
+    res["moe_ffn_per_tensor_4096tok_h7168_e64_top8_i2048"] = {
         "ms": round(med, 4), "ms_best": round(best, 4), "tflops": round(flops / med / 1e9, 2),
         "frac_mfma": round(flops / med / 1e9 / FP8_DENSE_PEAK_TFLOPS, 4)}
     return res

@@ -295,15 +295,57 @@ FP8G_API fp8g_status_t fp8_moe_fc1_silu_quant(const void* a, const float* a_scal
                                      int32_t gran_k, void* stream);
 
 /*
- * out[t] = bf16( sum_s topk_weights[t][s] * y[row_of_entry[t][s]] ), summed in FP32 in slot
- * order; entries with row_of_entry = -1 contribute nothing.
+ * out[t] = round( sum_s w[t][s] * y[row_of_entry[t][s]] ), summed in FP32 in slot order, rounded to
+ * BF16 or FP16 (out_dtype); entries with row_of_entry = -1 contribute nothing.
  *   y             (m_alloc, hidden) BF16 (the fc2 output)
- *   row_of_entry  (num_tokens, top_k) int32;  topk_weights (num_tokens, top_k) FP32
- *   out           (num_tokens, hidden) BF16, fully written
+ *   row_of_entry  (num_tokens, top_k) int32
+ *   topk_weights  (num_tokens, top_k) FP32 routing weights, or null for weight 1 (the per-tensor
+ *                 fused-MoE call of the flashinfer-rs README takes no routing weights)
+ *   out           (num_tokens, hidden) BF16 or FP16, fully written
  */
 FP8G_API fp8g_status_t fp8_moe_combine(const void* y, const int32_t* row_of_entry,
                               const float* topk_weights, int64_t num_tokens, int64_t top_k,
-                              int64_t hidden, int64_t m_alloc, void* out, void* stream);
+                              int64_t hidden, int64_t m_alloc, void* out, int32_t out_dtype,
+                              void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Per-tensor FP8 expert FFN (flashinfer-rs README, section "API Example: Fused MoE FP8 (cudarc)",
+ * per-tensor FP8 mode): FP8 tokens, one dequantisation scale per expert and GEMM, one (or one per
+ * expert) quantisation scale for fc2's input. The permutation and the combine are the calls above.
+ * ------------------------------------------------------------------------------------------- */
+
+/*
+ * out[i] = round( b_dequant[e] * (a[r_i] @ b[e].T) ) for every row with e = m_indices[i] >= 0,
+ * where r_i = a_rows[i] (a_rows non-null) or i; the sum is FP32 over all of k, one multiply by the
+ * expert's scale, BF16 or FP16 output (out_dtype). Rows with m_indices < 0 are not written.
+ *   a (a_rows_total, k) E4M3 (a_rows_total = m without a_rows); b (num_groups, n, k) E4M3;
+ *   b_dequant (num_groups,) FP32; m_indices (m,) int32 in 128-row-aligned regions; out (m, n)
+ * m, n and k are multiples of 128.
+ */
+FP8G_API fp8g_status_t fp8_group_gemm_contiguous_per_tensor(const void* a, int64_t a_rows_total,
+                                                   const int32_t* a_rows, const void* b,
+                                                   const float* b_dequant, const int32_t* m_indices,
+                                                   void* out, int32_t out_dtype, int64_t m, int64_t n,
+                                                   int64_t k, int64_t num_groups, void* stream);
+
+/*
+ * fc1 of the per-tensor FFN with the activation and fc2's input quantisation in its epilogue:
+ *   g, u = fc1_dequant[e] * (a[r_i] @ w1[e][0:inter].T),  fc1_dequant[e] * (a[r_i] @ w1[e][inter:].T)
+ *   q_out[i] = E4M3_RNE(saturate(silu(g) * u * fc2_quant[e or 0]))     (all FP32; +-448, NaN kept)
+ * fc2_quant holds one value (fc2_quant_per_expert = 0) or one per expert (= 1): a multiplicative
+ * quantisation scale, the convention of the MATE page's quant_scale (section "Attention",
+ * mla_rope_quantize_fp8). Rows with m_indices < 0 are not written.
+ *   a (a_rows_total, hidden) E4M3 tokens; w1 (num_experts, 2*inter, hidden) E4M3, gate then up;
+ *   fc1_dequant (num_experts,) FP32; q_out (m, inter) E4M3
+ * inter and hidden are multiples of 128; m of 128.
+ */
+FP8G_API fp8g_status_t fp8_moe_fc1_silu_quant_per_tensor(const void* a, int64_t a_rows_total,
+                                                 const int32_t* a_rows, const void* w1,
+                                                 const float* fc1_dequant, const float* fc2_quant,
+                                                 int32_t fc2_quant_per_expert,
+                                                 const int32_t* m_indices, void* q_out, int64_t m,
+                                                 int64_t inter, int64_t hidden,
+                                                 int64_t num_experts, void* stream);
 
 #ifdef __cplusplus
 }

@@ -19,12 +19,16 @@ from .gemm import (  # noqa: F401
     group_deepgemm_fp8_nt_groupwise,
 )
 from .moe import (  # noqa: F401
+    MoePerTensorWorkspace,
     MoeWorkspace,
     default_m_alloc,
     moe_build_permutation,
+    fp8_group_gemm_contiguous_per_tensor,
     moe_combine,
     moe_fc1_silu_quant,
+    moe_fc1_silu_quant_per_tensor,
     moe_ffn_fp8_block_scale,
+    moe_ffn_fp8_per_tensor,
     moe_gather_quant,
     moe_silu_mul_quant,
 )

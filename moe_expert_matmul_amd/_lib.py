@@ -41,7 +41,9 @@ SIGNATURES = {
     "fp8_moe_silu_mul_quant": ([_P, _P, _I64, _I64, _P, _P, _P], _I32),
     "fp8_moe_fc1_silu_quant": ([_P, _P, _I64, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32,
                                 _P], _I32),
-    "fp8_moe_combine": ([_P, _P, _P, _I64, _I64, _I64, _I64, _P, _P], _I32),
+    "fp8_moe_combine": ([_P, _P, _P, _I64, _I64, _I64, _I64, _P, _I32, _P], _I32),
+    "fp8_group_gemm_contiguous_per_tensor": ([_P, _I64, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _P], _I32),
+    "fp8_moe_fc1_silu_quant_per_tensor": ([_P, _I64, _P, _P, _P, _P, _I32, _P, _P, _I64, _I64, _I64, _I64, _P], _I32),
 }
 
 

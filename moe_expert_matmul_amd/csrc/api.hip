@@ -240,8 +240,11 @@ void group_gemm_contiguous(const void* a, const float* a_scale, int64_t a_src_ro
                            const void* b, const float* b_scale, const int32_t* m_indices, void* out, int64_t m,
                            int64_t n, int64_t k, int64_t num_groups, int32_t scale_major, int32_t gran_m,
                            int32_t gran_n, int32_t gran_k, void* stream, const char* what,
-                           int32_t out_dtype = FP8G_OUT_BF16, void* q_out = nullptr, float* q_scale_out = nullptr) {
+                           int32_t out_dtype = FP8G_OUT_BF16, void* q_out = nullptr, float* q_scale_out = nullptr,
+                           const float* group_dequant = nullptr, const float* act_quant = nullptr,
+                           int32_t act_quant_per_group = 0) {
   const bool swiglu = q_out != nullptr;
+  const bool pt = group_dequant != nullptr;  // per-tensor FP8: one dequantisation scale per group
   check_out_dtype(out_dtype);
   check_gemm_dims(m, n, k);
   check_gemm_dims(a_src_rows, n, k);
@@ -250,14 +253,24 @@ void group_gemm_contiguous(const void* a, const float* a_scale, int64_t a_src_ro
   check_scale_major(scale_major);
   check_granularity(gran_m, gran_n, gran_k);
   if (m == 0 || n == 0 || num_groups == 0) return;
-  check_operands(a, b, a_scale, b_scale, swiglu ? q_out : out, k);
+  if (pt) {
+    require((swiglu ? q_out : out) != nullptr, "the output must be non-null");
+    require(k == 0 || (a && b), "a and b must be non-null");
+    require(aligned(a, 16) && aligned(b, 16) && aligned(swiglu ? q_out : out, 16),
+            "a, b and the output must be 16-byte aligned");
+    require(aligned(group_dequant, 4), "the dequantisation scales must be 4-byte aligned");
+    if (swiglu) require(act_quant != nullptr && aligned(act_quant, 4), "fc2_quant must be non-null and 4-byte aligned");
+  } else {
+    check_operands(a, b, a_scale, b_scale, swiglu ? q_out : out, k);
+  }
   require(m_indices != nullptr && aligned(m_indices, 4), "m_indices must be non-null and 4-byte aligned");
   require(a_rows == nullptr || aligned(a_rows, 4), "a_rows must be 4-byte aligned");
-  if (swiglu) {
+  if (swiglu && !pt) {
     require(n % 256 == 0, "2*inter (%lld) must be a multiple of 256", (long long)n);
     require(q_scale_out != nullptr && aligned(q_scale_out, 4) && aligned(q_out, 16),
             "q_out must be 16-byte aligned and q_scale_out non-null and 4-byte aligned");
   }
+  if (swiglu) require(n % 256 == 0, "2*inter (%lld) must be a multiple of 256", (long long)n);
   require(k == 0 || a_src_rows > 0, "a must have at least one row");
   check_device();
   fp8g::GemmParams p{};
@@ -272,6 +285,9 @@ void group_gemm_contiguous(const void* a, const float* a_scale, int64_t a_src_ro
   p.inter = (int32_t)(n / 2);
   p.q_out = static_cast<uint8_t*>(q_out);
   p.q_scale_out = q_scale_out;
+  p.group_dequant = group_dequant;
+  p.act_quant = act_quant;
+  p.act_quant_per_group = act_quant_per_group;
   p.a_src_rows = (int32_t)a_src_rows;
   p.m = (int32_t)m;
   p.n = (int32_t)n;
@@ -297,8 +313,9 @@ void group_gemm_contiguous(const void* a, const float* a_scale, int64_t a_src_ro
   p.group_m = fp8g::tile_rows(cfg) == 256 ? 1 : p.tiles_m;
   const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
   require(grid <= kInt32Max, "too many tiles");
-  check_hip(fp8g::launch_gemm(swiglu ? fp8g::MODE_CONTIG_SWIGLU : fp8g::MODE_CONTIG, cfg, p, (int)grid,
-                              (hipStream_t)stream), what);
+  const fp8g::GemmMode mode = pt ? (swiglu ? fp8g::MODE_CONTIG_PT_SWIGLU : fp8g::MODE_CONTIG_PT)
+                                 : (swiglu ? fp8g::MODE_CONTIG_SWIGLU : fp8g::MODE_CONTIG);
+  check_hip(fp8g::launch_gemm(mode, cfg, p, (int)grid, (hipStream_t)stream), what);
 }
 
 }  // namespace
@@ -346,6 +363,40 @@ fp8g_status_t fp8_moe_fc1_silu_quant(const void* a, const float* a_scale, int64_
     group_gemm_contiguous(a, a_scale, a_rows == nullptr ? m : a_rows_total, a_rows, w1, w1_scale, m_indices, nullptr,
                           m, 2 * inter, hidden, num_experts, scale_major, gran_m, gran_n, gran_k, stream,
                           "fp8_moe_fc1_silu_quant launch", FP8G_OUT_BF16, q_out, q_scale_out);
+  });
+}
+
+fp8g_status_t fp8_group_gemm_contiguous_per_tensor(const void* a, int64_t a_rows_total, const int32_t* a_rows,
+                                                  const void* b, const float* b_dequant, const int32_t* m_indices,
+                                                  void* out, int32_t out_dtype, int64_t m, int64_t n, int64_t k,
+                                                  int64_t num_groups, void* stream) {
+  return guarded([&] {
+    if (m > 0 && n > 0 && num_groups > 0) require(b_dequant != nullptr, "b_dequant must be non-null");
+    group_gemm_contiguous(a, nullptr, a_rows == nullptr ? m : a_rows_total, a_rows, b, nullptr, m_indices, out, m, n,
+                          k, num_groups, FP8G_SCALE_K_MAJOR, 1, 128, 128, stream,
+                          "fp8_group_gemm_contiguous_per_tensor launch", out_dtype, nullptr, nullptr, b_dequant);
+  });
+}
+
+fp8g_status_t fp8_moe_fc1_silu_quant_per_tensor(const void* a, int64_t a_rows_total, const int32_t* a_rows,
+                                                const void* w1, const float* fc1_dequant, const float* fc2_quant,
+                                                int32_t fc2_quant_per_expert, const int32_t* m_indices, void* q_out,
+                                                int64_t m, int64_t inter, int64_t hidden, int64_t num_experts,
+                                                void* stream) {
+  return guarded([&] {
+    require(inter >= 0 && inter <= kInt32Max / 2, "inter must be in [0, 2^30)");
+    require(inter % 128 == 0, "inter (%lld) must be a multiple of 128", (long long)inter);
+    require(fc2_quant_per_expert == 0 || fc2_quant_per_expert == 1, "fc2_quant_per_expert must be 0 or 1");
+    if (m == 0 || inter == 0 || num_experts == 0) {
+      check_gemm_dims(m, 2 * inter, hidden);
+      return;
+    }
+    require(q_out != nullptr, "q_out must be non-null");
+    require(fc1_dequant != nullptr, "fc1_dequant must be non-null");
+    group_gemm_contiguous(a, nullptr, a_rows == nullptr ? m : a_rows_total, a_rows, w1, nullptr, m_indices, nullptr, m,
+                          2 * inter, hidden, num_experts, FP8G_SCALE_K_MAJOR, 1, 128, 128, stream,
+                          "fp8_moe_fc1_silu_quant_per_tensor launch", FP8G_OUT_BF16, q_out, nullptr, fc1_dequant,
+                          fc2_quant, fc2_quant_per_expert);
   });
 }
 
@@ -572,20 +623,21 @@ fp8g_status_t fp8_moe_silu_mul_quant(const void* y, const int32_t* m_indices, in
 
 fp8g_status_t fp8_moe_combine(const void* y, const int32_t* row_of_entry,
                               const float* topk_weights, int64_t num_tokens, int64_t top_k,
-                              int64_t hidden, int64_t m_alloc, void* out, void* stream) {
+                              int64_t hidden, int64_t m_alloc, void* out, int32_t out_dtype, void* stream) {
   return guarded([&] {
     require(num_tokens >= 0 && top_k >= 0 && hidden >= 0 && m_alloc >= 0, "sizes must be non-negative");
     require(hidden % 128 == 0, "hidden (%lld) must be a multiple of 128", (long long)hidden);
     require(num_tokens <= kInt32Max && top_k <= 64 && hidden <= kInt32Max && m_alloc <= kInt32Max,
             "sizes out of range (top_k must be at most 64)");
+    check_out_dtype(out_dtype);
     if (num_tokens == 0 || hidden == 0) return;
-    require(out && (top_k == 0 || (y && row_of_entry && topk_weights)), "pointers must be non-null");
+    require(out && (top_k == 0 || (y && row_of_entry)), "pointers must be non-null");
     require(aligned(y, 16) && aligned(out, 16) && aligned(row_of_entry, 4) && aligned(topk_weights, 4),
             "y and out must be 16-byte aligned, row_of_entry and topk_weights 4-byte aligned");
     check_device();
     check_hip(fp8g::launch_moe_combine(static_cast<const uint16_t*>(y), row_of_entry, topk_weights,
                                        (int)num_tokens, (int)top_k, (int)hidden, (int)m_alloc,
-                                       static_cast<uint16_t*>(out), (hipStream_t)stream),
+                                       static_cast<uint16_t*>(out), out_dtype == FP8G_OUT_FP16, (hipStream_t)stream),
               "fp8_moe_combine launch");
   });
 }

@@ -133,12 +133,50 @@ __device__ __forceinline__ void swiglu_epilogue(const GemmParams& p, const f32x4
   }
 }
 
+// Epilogue of the per-tensor expert FFN's fc1 (CONTIG_PT_SWIGLU): gate and up are the FP32 sums
+// times the expert's dequantisation scale, h = silu(gate) * up in FP32 (silu(g) = g / (1 + exp(-g))),
+// and the code is E4M3_RNE(saturate(h * act_quant)) -- one per-tensor (or per-expert) scale, so no
+// row maximum and no exchange between waves. Column mapping as in swiglu_epilogue.
+template <typename T, int WN>
+__device__ __forceinline__ void swiglu_pt_epilogue(const GemmParams& p, const f32x4 (&acc)[T::IG][T::JG], int row0,
+                                                   int row_end, int bsel, int tn, int i0, int wave, int lane,
+                                                   bool wave_live) {
+  if (!wave_live) return;
+  constexpr int OUTW = 128 / WN;
+  constexpr int HALF = T::JG / 2;
+  const int fr = lane & 15, q = wave % WN;
+  const int cl = (lane >> 4) * 4;
+  const float d = p.group_dequant[bsel];
+  const float qs = p.act_quant[p.act_quant_per_group ? bsel : 0];
+#pragma unroll
+  for (int ig = 0; ig < T::IG; ++ig) {
+    const int i = row0 + i0 + ig * 16 + fr;
+    if (i >= row_end || p.rowinfo[i] != bsel) continue;
+    uint8_t* orow = p.q_out + (int64_t)i * p.inter + 128 * tn + q * OUTW;
+#pragma unroll
+    for (int jg = 0; jg < HALF; ++jg) {
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float g = acc[ig][jg][r] * d, u = acc[ig][HALF + jg][r] * d;
+        v[r] = __fdiv_rn(g, 1.0f + expf(-g)) * u * qs;
+        if (!(fabsf(v[r]) <= kE4M3MaxOut) && v[r] == v[r]) v[r] = copysignf(kE4M3MaxOut, v[r]);  // saturate
+      }
+      int w4 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+      w4 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w4, true);
+      *reinterpret_cast<int*>(orow + jg * 16 + cl) = w4;
+    }
+  }
+}
+
 template <int BM, int BN, int WM, int WN, int STAGES, int MODE>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_fp8_groupwise_kernel(const GemmParams p) {
   using T = Tile<BM, BN, WM, WN, STAGES>;
-  constexpr bool CONTIG = MODE == MODE_CONTIG || MODE == MODE_CONTIG_SWIGLU;
-  constexpr bool SWIGLU = MODE == MODE_CONTIG_SWIGLU;
+  constexpr bool PT = MODE == MODE_CONTIG_PT || MODE == MODE_CONTIG_PT_SWIGLU;
+  constexpr bool CONTIG = MODE == MODE_CONTIG || MODE == MODE_CONTIG_SWIGLU || PT;
+  constexpr bool SWIGLU = MODE == MODE_CONTIG_SWIGLU || MODE == MODE_CONTIG_PT_SWIGLU;
+  constexpr bool NO_PROMOTION = MODE == MODE_BMM || PT;  // scales constant along K: applied at the end
   // SWIGLU: wave column q of the WN holds the gate and the up columns of OUTW output columns; its
   // b rows ("virtual columns" v of the tile) are OUTW gate rows then OUTW up rows.
   constexpr int OUTW = SWIGLU ? 128 / WN : 0;
@@ -308,7 +346,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     } else {
       // BMM: the scales act in the epilogue; the load still runs (through rNone) so that every
       // mode issues the same loads per K block
-      load_lds_4(live && MODE != MODE_BMM ? rS : rNone, sA + s_dst, s_voff, (uint32_t)kb * s_kb_bytes);
+      load_lds_4(live && !NO_PROMOTION ? rS : rNone, sA + s_dst, s_voff, (uint32_t)kb * s_kb_bytes);
     }
   };
   auto issue_loads = [&](int kb, bool live) {
@@ -427,7 +465,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     lds_pipeline_barrier();
     const int kb_load = kb + STAGES - 1;
     if (wave_live) {
-      if constexpr (MODE == MODE_BMM)
+      if constexpr (NO_PROMOTION)
         compute_bmm(kb, kb_load, kb_load < KB);
       else
         compute(kb, kb_load, kb_load < KB);
@@ -436,7 +474,10 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   }
   wait_vmcnt<0>();  // the zero-fill loads of the last iterations
 
-  if constexpr (SWIGLU) {
+  if constexpr (MODE == MODE_CONTIG_PT_SWIGLU) {
+    swiglu_pt_epilogue<T, WN>(p, acc, row0, row_end, bsel, tn, i0, wave, lane, wave_live);
+    return;
+  } else if constexpr (SWIGLU) {
     swiglu_epilogue<T, WN>(p, acc, smem, row0, row_end, bsel, tn, i0, wave, lane, wave_live);
     return;
   }
@@ -448,6 +489,15 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   if (wave_live) {
   const int jl = (lane >> 4) * 4;
   const bool vec = (p.n & 3) == 0;
+  if constexpr (MODE == MODE_CONTIG_PT) {
+    const float d = p.group_dequant[bsel];
+#pragma unroll
+    for (int ig = 0; ig < T::IG; ++ig)
+#pragma unroll
+      for (int jg = 0; jg < T::JG; ++jg)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[ig][jg][r] *= d;
+  }
   if constexpr (MODE == MODE_BMM) {
     // out = sa * sb * acc in FP32 (one rounding per product), before the output rounding
     const float* SAg = p.sa + (p.bmm_sa_rows ? (int64_t)g * p.m : 0);
@@ -550,6 +600,16 @@ hipError_t launch_cfg(GemmMode mode, const GemmParams& p, int grid, hipStream_t 
     case MODE_BMM:
       hipLaunchKernelGGL((gemm_fp8_groupwise_kernel<BM, BN, WM, WN, STAGES, MODE_BMM>), dim3(grid), block, 0, stream, p);
       break;
+    case MODE_CONTIG_PT:
+      hipLaunchKernelGGL((gemm_fp8_groupwise_kernel<BM, BN, WM, WN, STAGES, MODE_CONTIG_PT>), dim3(grid), block, 0, stream, p);
+      break;
+    case MODE_CONTIG_PT_SWIGLU:
+      if constexpr (BN == 256) {
+        hipLaunchKernelGGL((gemm_fp8_groupwise_kernel<BM, BN, WM, WN, STAGES, MODE_CONTIG_PT_SWIGLU>), dim3(grid), block,
+                           0, stream, p);
+        break;
+      }
+      return hipErrorInvalidValue;
     case MODE_CONTIG_SWIGLU:
       if constexpr (BN == 256) {
         hipLaunchKernelGGL((gemm_fp8_groupwise_kernel<BM, BN, WM, WN, STAGES, MODE_CONTIG_SWIGLU>), dim3(grid), block, 0,

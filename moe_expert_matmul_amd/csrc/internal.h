@@ -13,6 +13,8 @@ enum GemmMode : int {
   MODE_MASKED = 2,  // per group g, rows below masked_m[g]
   MODE_CONTIG_SWIGLU = 3,  // contiguous, epilogue silu(gate) * up -> 1x128 E4M3 (expert-FFN fc1)
   MODE_BMM = 4,     // per batch g: out = sa * sb * (a @ b.T), scales per tensor or per row / column
+  MODE_CONTIG_PT = 5,         // contiguous, out = group_dequant[e] * (a @ b[e].T) (per-tensor FP8)
+  MODE_CONTIG_PT_SWIGLU = 6,  // contiguous per-tensor, epilogue E4M3(silu(gate) * up * act_quant)
 };
 
 // Everything the GEMM kernel needs, passed by value as the kernel argument. Strides in elements.
@@ -34,6 +36,11 @@ struct GemmParams {
   // BMM: a_scale holds one value (0) or one per row of each batch (1); b_scale one value or one per
   // column of each batch; scale groups are m (a) and n (b) values apart.
   int32_t bmm_sa_rows, bmm_sb_cols;
+  // CONTIG_PT(_SWIGLU): one dequantisation scale per group (expert) applied to the FP32 sum; the
+  // SWIGLU form multiplies h by act_quant[e] (act_quant_per_group) or act_quant[0] and writes E4M3.
+  const float* group_dequant;
+  const float* act_quant;
+  int32_t act_quant_per_group;
   int32_t inter;
   uint8_t* q_out;
   float* q_scale_out;
@@ -87,6 +94,6 @@ hipError_t launch_moe_silu_mul_quant(const uint16_t* y, const int32_t* m_indices
                                      hipStream_t stream);
 hipError_t launch_moe_combine(const uint16_t* y, const int32_t* row_of_entry,
                               const float* topk_weights, int num_tokens, int top_k, int hidden,
-                              int m_alloc, uint16_t* out, hipStream_t stream);
+                              int m_alloc, uint16_t* out, bool out_fp16, hipStream_t stream);
 
 }  // namespace fp8g

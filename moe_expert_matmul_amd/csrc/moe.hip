@@ -157,10 +157,10 @@ constexpr int kCombineBatch = 8;
 __global__ void __launch_bounds__(1024)
 moe_combine_kernel(const uint16_t* __restrict__ y, const int32_t* __restrict__ row_of_entry,
                    const float* __restrict__ weights, int top_k, int hidden, int m_alloc,
-                   uint16_t* __restrict__ out) {
+                   uint16_t* __restrict__ out, bool out_fp16) {
   const int t = blockIdx.x;
   const int32_t* rows = row_of_entry + (int64_t)t * top_k;
-  const float* w = weights + (int64_t)t * top_k;
+  const float* w = weights != nullptr ? weights + (int64_t)t * top_k : nullptr;  // null: weight 1
   for (int c = threadIdx.x * 8; c < hidden; c += blockDim.x * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < top_k; s0 += kCombineBatch) {
@@ -175,7 +175,7 @@ moe_combine_kernel(const uint16_t* __restrict__ y, const int32_t* __restrict__ r
 #pragma unroll
       for (int j = 0; j < kCombineBatch; ++j) {
         if (!live[j]) continue;
-        const float ws = w[s0 + j];
+        const float ws = w != nullptr ? w[s0 + j] : 1.0f;
         float v[8];
         unpack_bf16x8(raw[j], v);
 #pragma unroll
@@ -183,10 +183,17 @@ moe_combine_kernel(const uint16_t* __restrict__ y, const int32_t* __restrict__ r
       }
     }
     uint4 o;
-    o.x = pack_bf16x2(acc[0], acc[1]);
-    o.y = pack_bf16x2(acc[2], acc[3]);
-    o.z = pack_bf16x2(acc[4], acc[5]);
-    o.w = pack_bf16x2(acc[6], acc[7]);
+    if (out_fp16) {
+      o.x = pack_f16x2(acc[0], acc[1]);
+      o.y = pack_f16x2(acc[2], acc[3]);
+      o.z = pack_f16x2(acc[4], acc[5]);
+      o.w = pack_f16x2(acc[6], acc[7]);
+    } else {
+      o.x = pack_bf16x2(acc[0], acc[1]);
+      o.y = pack_bf16x2(acc[2], acc[3]);
+      o.z = pack_bf16x2(acc[4], acc[5]);
+      o.w = pack_bf16x2(acc[6], acc[7]);
+    }
     *reinterpret_cast<uint4*>(out + (int64_t)t * hidden + c) = o;
   }
 }
@@ -221,10 +228,10 @@ hipError_t launch_moe_silu_mul_quant(const uint16_t* y, const int32_t* m_indices
 
 hipError_t launch_moe_combine(const uint16_t* y, const int32_t* row_of_entry,
                               const float* topk_weights, int num_tokens, int top_k, int hidden,
-                              int m_alloc, uint16_t* out, hipStream_t stream) {
+                              int m_alloc, uint16_t* out, bool out_fp16, hipStream_t stream) {
   const int threads = std::min(1024, (hidden / 8 + 63) / 64 * 64);
   hipLaunchKernelGGL(moe_combine_kernel, dim3(num_tokens), dim3(threads), 0, stream, y, row_of_entry,
-                     topk_weights, top_k, hidden, m_alloc, out);
+                     topk_weights, top_k, hidden, m_alloc, out, out_fp16);
   return hipGetLastError();
 }
 

@@ -31,6 +31,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  const f16x2_t v = {(_Float16)a, (_Float16)b};  // round-to-nearest-even
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // Quantise the 8 values a lane holds, given the amax of its 16-lane team; writes 8 codes + scale.
 __device__ __forceinline__ void quant_store_8(const float v[8], float amax, uint8_t* codes_out, float* scale_out,
                                               bool write_scale) {

@@ -18,8 +18,8 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from .gemm import (_FP8_DTYPES, _GRAN, _check, _major, _ptr, _require_cuda, _stream, fp8_group_gemm_contiguous,
-                   fp8_group_gemm_contiguous_gather)
+from .gemm import (_FP8_DTYPES, _GRAN, _OUT_DTYPES, _check, _major, _out_code, _ptr, _require_cuda, _stream,
+                   fp8_group_gemm_contiguous, fp8_group_gemm_contiguous_gather)
 
 
 def default_m_alloc(num_tokens: int, top_k: int, num_experts: int) -> int:
@@ -140,16 +140,19 @@ def moe_fc1_silu_quant(a, a_scale, a_rows, w1, w1_scale, m_indices, q_out, q_sca
 
 
 def moe_combine(y, row_of_entry, topk_weights, out):
+    """out (T, hidden) bf16 or fp16 = sum over slots of topk_weights * y[row_of_entry] (weight 1 when
+    topk_weights is None)."""
     dev = _require_cuda(y)
     m_alloc, h = y.shape
     t, k = row_of_entry.shape
     _check(y, "y", (torch.bfloat16,), (m_alloc, h), dev)
     _check(row_of_entry, "row_of_entry", (torch.int32,), (t, k), dev)
-    _check(topk_weights, "topk_weights", (torch.float32,), (t, k), dev)
-    _check(out, "out", (torch.bfloat16,), (t, h), dev)
+    if topk_weights is not None:
+        _check(topk_weights, "topk_weights", (torch.float32,), (t, k), dev)
+    _check(out, "out", _OUT_DTYPES, (t, h), dev)
     with torch.cuda.device(dev):
-        st = _lib.load().fp8_moe_combine(y.data_ptr(), row_of_entry.data_ptr(), topk_weights.data_ptr(), t, k, h,
-                                         m_alloc, out.data_ptr(), _stream(dev))
+        st = _lib.load().fp8_moe_combine(y.data_ptr(), row_of_entry.data_ptr(), _ptr(topk_weights), t, k, h,
+                                         m_alloc, out.data_ptr(), _out_code(out), _stream(dev))
     _lib.check(st, "fp8_moe_combine")
 
 
@@ -176,5 +179,110 @@ def moe_ffn_fp8_block_scale(x, topk_ids, topk_weights, w1, s1, w2, s2, out=None,
         fp8_group_gemm_contiguous_gather(ws.a1, ws.sa1, ws.src_token, w1, s1, ws.m_indices, ws.y1)
         moe_silu_mul_quant(ws.y1, ws.m_indices, ws.a2, ws.sa2)
     fp8_group_gemm_contiguous(ws.a2, w2, ws.sa2, s2, ws.m_indices, ws.y2)
+    moe_combine(ws.y2, ws.row_of_entry, topk_weights, out)
+    return out
+
+
+# ---- per-tensor FP8 expert FFN ----------------------------------------------------------------------
+
+
+@dataclass
+class MoePerTensorWorkspace:
+    """Device buffers of one per-tensor expert-FFN call (allocated once, reused across calls)."""
+
+    m_indices: torch.Tensor
+    src_token: torch.Tensor
+    row_of_entry: torch.Tensor
+    a2: torch.Tensor  # fc2's E4M3 input, written by fc1's epilogue
+    y2: torch.Tensor
+
+    @staticmethod
+    def allocate(num_tokens, top_k, num_experts, hidden, inter, device) -> "MoePerTensorWorkspace":
+        m_alloc = default_m_alloc(num_tokens, top_k, num_experts)
+        e = dict(device=device)
+        return MoePerTensorWorkspace(
+            m_indices=torch.empty(m_alloc, dtype=torch.int32, **e),
+            src_token=torch.empty(m_alloc, dtype=torch.int32, **e),
+            row_of_entry=torch.empty((num_tokens, top_k), dtype=torch.int32, **e),
+            a2=torch.empty((m_alloc, inter), dtype=torch.uint8, **e),
+            y2=torch.empty((m_alloc, hidden), dtype=torch.bfloat16, **e),
+        )
+
+    @property
+    def m_alloc(self) -> int:
+        return self.m_indices.shape[0]
+
+
+def fp8_group_gemm_contiguous_per_tensor(a, a_rows, b, b_dequant, m_indices, out):
+    """out[i] = b_dequant[e] * (a[a_rows[i]] @ b[e].T) for rows with e = m_indices[i] >= 0 (a_rows None:
+    row i of a); FP32 sum over k, bf16 or fp16 out."""
+    dev = _require_cuda(a)
+    rows_total, k = a.shape
+    m = m_indices.shape[0]
+    groups, n, _ = b.shape
+    _check(a, "a", _FP8_DTYPES, (rows_total, k), dev)
+    if a_rows is not None:
+        _check(a_rows, "a_rows", (torch.int32,), (m,), dev)
+    _check(b, "b", _FP8_DTYPES, (groups, n, k), dev)
+    _check(b_dequant, "b_dequant", (torch.float32,), (groups,), dev)
+    _check(m_indices, "m_indices", (torch.int32,), (m,), dev)
+    _check(out, "out", _OUT_DTYPES, (m, n), dev)
+    with torch.cuda.device(dev):
+        st = _lib.load().fp8_group_gemm_contiguous_per_tensor(_ptr(a), rows_total, _ptr(a_rows), _ptr(b),
+                                                              _ptr(b_dequant), _ptr(m_indices), _ptr(out),
+                                                              _out_code(out), m, n, k, groups, _stream(dev))
+    _lib.check(st, "fp8_group_gemm_contiguous_per_tensor")
+    return out
+
+
+def moe_fc1_silu_quant_per_tensor(a, a_rows, w1, fc1_dequant, fc2_quant, m_indices, q_out):
+    """q_out = E4M3(saturate(silu(gate) * up * fc2_quant)), gate/up = fc1_dequant[e] * (a[a_rows] @ w1[e].T)
+    halves; fc2_quant holds one value or one per expert."""
+    dev = _require_cuda(a)
+    rows_total, hidden = a.shape
+    m = m_indices.shape[0]
+    num_experts, two_inter, _ = w1.shape
+    inter = two_inter // 2
+    _check(a, "a", _FP8_DTYPES, (rows_total, hidden), dev)
+    if a_rows is not None:
+        _check(a_rows, "a_rows", (torch.int32,), (m,), dev)
+    _check(w1, "w1", _FP8_DTYPES, (num_experts, 2 * inter, hidden), dev)
+    _check(fc1_dequant, "fc1_dequant", (torch.float32,), (num_experts,), dev)
+    if fc2_quant.numel() not in (1, num_experts):
+        raise ValueError(f"fc2_quant must hold 1 or {num_experts} values, got {fc2_quant.numel()}")
+    _check(fc2_quant, "fc2_quant", (torch.float32,), tuple(fc2_quant.shape), dev)
+    _check(m_indices, "m_indices", (torch.int32,), (m,), dev)
+    _check(q_out, "q_out", _FP8_DTYPES, (m, inter), dev)
+    per_expert = int(fc2_quant.numel() == num_experts and num_experts > 1)
+    with torch.cuda.device(dev):
+        st = _lib.load().fp8_moe_fc1_silu_quant_per_tensor(_ptr(a), rows_total, _ptr(a_rows), _ptr(w1),
+                                                           _ptr(fc1_dequant), _ptr(fc2_quant), per_expert,
+                                                           _ptr(m_indices), _ptr(q_out), m, inter, hidden,
+                                                           num_experts, _stream(dev))
+    _lib.check(st, "fp8_moe_fc1_silu_quant_per_tensor")
+    return q_out
+
+
+def moe_ffn_fp8_per_tensor(x_fp8, topk_ids, w1, w2, fc1_dequant, fc2_quant, fc2_dequant, fc1_input_dequant=None,
+                           topk_weights=None, out=None, out_dtype=torch.bfloat16, workspace=None):
+    """Per-tensor FP8 expert FFN with the argument list of the flashinfer-rs README (section "API
+    Example: Fused MoE FP8 (cudarc)", per-tensor FP8 mode): x_fp8 (T, hidden) E4M3 tokens, topk_ids
+    (T, top_k) int32, w1 (E, 2*inter, hidden) gate then up, w2 (E, hidden, inter), fc1_dequant (E,),
+    fc2_quant (1 or E,), fc2_dequant (E,), out (T, hidden) bf16 or fp16. ``fc1_input_dequant`` (the
+    tokens' own scale, already a factor of fc1_dequant) is accepted and not applied; the README's call
+    takes no routing weights, so the expert outputs are summed with weight 1 unless ``topk_weights``
+    is given. Four library calls: permutation -> fc1 + SiLU-mul + quantise -> fc2 -> combine."""
+    num_tokens, hidden = x_fp8.shape
+    num_experts, two_inter, _ = w1.shape
+    inter = two_inter // 2
+    top_k = topk_ids.shape[1]
+    if w2.shape != (num_experts, hidden, inter):
+        raise ValueError(f"w2 has shape {tuple(w2.shape)}, expected {(num_experts, hidden, inter)}")
+    ws = workspace or MoePerTensorWorkspace.allocate(num_tokens, top_k, num_experts, hidden, inter, x_fp8.device)
+    if out is None:
+        out = torch.empty((num_tokens, hidden), dtype=out_dtype, device=x_fp8.device)
+    moe_build_permutation(topk_ids, num_experts, ws.m_indices, ws.src_token, ws.row_of_entry)
+    moe_fc1_silu_quant_per_tensor(x_fp8, ws.src_token, w1, fc1_dequant, fc2_quant, ws.m_indices, ws.a2)
+    fp8_group_gemm_contiguous_per_tensor(ws.a2, None, w2, fc2_dequant, ws.m_indices, ws.y2)
     moe_combine(ws.y2, ws.row_of_entry, topk_weights, out)
     return out

@@ -113,10 +113,12 @@ def silu_mul(y):
 
 
 def combine(y2, row_of_entry, topk_weights):
-    """out[t] = sum_slot w[t, slot] * y2[row_of_entry[t, slot]] in float64; row -1 adds nothing."""
+    """out[t] = sum_slot w[t, slot] * y2[row_of_entry[t, slot]] in float64; row -1 adds nothing.
+    ``topk_weights`` None means weight 1 (the per-tensor call of the flashinfer-rs README passes no
+    routing weights)."""
     y2 = np.asarray(y2, dtype=np.float64)
     rows = np.asarray(row_of_entry, dtype=np.int64)
-    w = np.asarray(topk_weights, dtype=np.float64)
+    w = np.ones(rows.shape) if topk_weights is None else np.asarray(topk_weights, dtype=np.float64)
     out = np.zeros((rows.shape[0], y2.shape[1]), dtype=np.float64)
     for slot in range(rows.shape[1]):
         r = rows[:, slot]
@@ -140,3 +142,64 @@ def moe_ffn(x, topk_ids, topk_weights, w1, s1, w2, s2, m_alloc=None):
     y2 = bf16.round_to_bf16(group_gemm_contiguous(a2, w2, sa2, s2, perm["m_indices"]))
     out = combine(np.nan_to_num(y2), perm["row_of_entry"], topk_weights)
     return dict(xq=xq, xs=xs, perm=perm, a1=a1, sa1=sa1, y1=y1, h=h, a2=a2, sa2=sa2, y2=y2, out=out)
+
+
+# ---- per-tensor FP8 mode (flashinfer-rs README, "API Example: Fused MoE FP8 (cudarc)", per-tensor) --
+#
+# Readings: the tokens arrive as E4M3 codes; fc1_dequant[e] and fc2_dequant[e] multiply the FP32
+# sums of fc1 and fc2 of expert e (they hold the product of the activation's and the weights'
+# scales, so fc1_input_dequant is not applied again); fc2_quant multiplies h before the E4M3 cast
+# (the page's multiplicative quant-scale convention), one value or one per expert; values beyond
+# +-448 saturate; fc1's value is not rounded to BF16 between the GEMM and the activation.
+
+
+def fc1_act_per_tensor(x_codes, src_token, m_indices, w1, fc1_dequant, fc2_quant):
+    """(h, q): h = silu(g) * u in float64 with g, u = fc1_dequant[e] * (x[src] @ w1[e] halves .T);
+    q = float32(h) * fc2_quant (float32, the precision the code is decided in); NaN on padding rows."""
+    x = np.asarray(x_codes)
+    m_idx = np.asarray(m_indices, dtype=np.int64)
+    src = np.asarray(src_token, dtype=np.int64)
+    w1 = np.asarray(w1)
+    inter = w1.shape[1] // 2
+    d1 = np.asarray(fc1_dequant, dtype=np.float32).astype(np.float64)
+    qs = np.asarray(fc2_quant, dtype=np.float32).reshape(-1)
+    h = np.full((m_idx.size, inter), np.nan)
+    q = np.full((m_idx.size, inter), np.nan, dtype=np.float32)
+    for e in np.unique(m_idx[m_idx >= 0]):
+        rows = np.nonzero(m_idx == e)[0]
+        y = (e4m3.decode(x[src[rows]]) @ e4m3.decode(w1[e]).T) * d1[e]    # exact sums, one scaling
+        h[rows] = silu_mul(y)
+        q[rows] = h[rows].astype(np.float32) * qs[e if qs.size > 1 else 0]
+    return h, q
+
+
+def quantize_per_tensor(q):
+    """E4M3 codes of float32 values already multiplied by their quantisation scale: saturated to
+    +-448, round to nearest even, NaN kept."""
+    q = np.asarray(q, dtype=np.float32)
+    return e4m3.encode_rne(np.where(np.isnan(q), q, np.clip(q, -e4m3.MAX_FINITE, e4m3.MAX_FINITE)).astype(np.float32))
+
+
+def fc2_per_tensor(a2_codes, m_indices, w2, fc2_dequant):
+    """fc2_dequant[e] * (a2[i] @ w2[e].T) in float64 for rows with e = m_indices[i] >= 0, NaN else."""
+    a2 = np.asarray(a2_codes)
+    m_idx = np.asarray(m_indices, dtype=np.int64)
+    w2 = np.asarray(w2)
+    d2 = np.asarray(fc2_dequant, dtype=np.float32).astype(np.float64)
+    out = np.full((m_idx.size, w2.shape[1]), np.nan)
+    for e in np.unique(m_idx[m_idx >= 0]):
+        rows = np.nonzero(m_idx == e)[0]
+        out[rows] = (e4m3.decode(a2[rows]) @ e4m3.decode(w2[e]).T) * d2[e]
+    return out
+
+
+def moe_ffn_per_tensor(x_codes, topk_ids, w1, w2, fc1_dequant, fc2_quant, fc2_dequant, topk_weights=None,
+                       m_alloc=None):
+    """All per-tensor stages chained on the oracle's own intermediates (fc2's output rounded to BF16,
+    the stored type, before the combine)."""
+    perm = build_permutation(topk_ids, np.asarray(w1).shape[0], m_alloc)
+    h, q = fc1_act_per_tensor(x_codes, perm["src_token"], perm["m_indices"], w1, fc1_dequant, fc2_quant)
+    a2 = quantize_per_tensor(np.nan_to_num(q))
+    y2 = bf16.round_to_bf16(fc2_per_tensor(a2, perm["m_indices"], w2, fc2_dequant))
+    out = combine(np.nan_to_num(y2), perm["row_of_entry"], topk_weights)
+    return dict(perm=perm, h=h, q=q, a2=a2, y2=y2, out=out)

@@ -131,7 +131,7 @@ def test_moe_steps_validate_sizes(lib):
     assert st == _lib.INVALID_ARGUMENT
     st, _ = _status(lib.fp8_moe_silu_mul_quant, P, P, 128, 100, P, P, None)
     assert st == _lib.INVALID_ARGUMENT
-    st, _ = _status(lib.fp8_moe_combine, P, P, P, 4, 65, 128, 128, P, None)
+    st, _ = _status(lib.fp8_moe_combine, P, P, P, 4, 65, 128, 128, P, 0, None)
     assert st == _lib.INVALID_ARGUMENT
 
 

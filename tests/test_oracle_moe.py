@@ -9,6 +9,7 @@ import torch
 
 import workloads
 from oracle import bf16, e4m3, moe
+from oracle import gemm as gemm_module
 from oracle.gemm import gemm_fp8_nt_groupwise
 
 
@@ -168,3 +169,75 @@ def test_workload_quantiser_blocks():
     assert not np.any((b & 0x7F) == 0x7F)
     dec = np.abs(e4m3.decode(b)).reshape(2, 128, 3, 128).max(axis=(1, 3))
     assert np.all(dec == 448.0)
+
+
+# ---- per-tensor FP8 mode -------------------------------------------------------------------------
+
+def test_per_tensor_fc1_activation_closed_form():
+    # all-ones codes, hidden 128, fc1_dequant 1/64: gate = up = 2, h = silu(2) * 2 = 4 / (1 + e^-2)
+    # = 3.5232, whose nearest E4M3 value is 3.5 (code 0x46; 3.75 is 0x47).
+    x = np.full((2, 128), 0x38, np.uint8)
+    w1 = np.full((1, 256, 128), 0x38, np.uint8)
+    h, q = moe.fc1_act_per_tensor(x, np.array([0, 1]), np.array([0, 0]), w1, np.array([1 / 64], np.float32),
+                                  np.array([1.0], np.float32))
+    assert np.allclose(h, 4.0 / (1.0 + math.exp(-2.0)), rtol=1e-15)
+    assert np.all(moe.quantize_per_tensor(q) == 0x46)
+    # a large quantisation scale saturates at 448 (0x7E)
+    _, q = moe.fc1_act_per_tensor(x, np.array([0, 1]), np.array([0, 0]), w1, np.array([1 / 64], np.float32),
+                                  np.array([1000.0], np.float32))
+    assert np.all(moe.quantize_per_tensor(q) == 0x7E)
+
+
+def test_per_tensor_fc1_gathers_rows_and_uses_each_experts_scales():
+    rng = np.random.default_rng(70)
+    x = rng.integers(0, 0x7E, (5, 256)).astype(np.uint8)
+    w1 = rng.integers(0, 0x7E, (2, 256, 256)).astype(np.uint8)
+    d1 = np.array([0.01, 0.02], np.float32)
+    qs = np.array([0.5, 2.0], np.float32)
+    src, m_idx = np.array([4, 0, -1, 2]), np.array([1, 0, -1, 1])
+    h, q = moe.fc1_act_per_tensor(x, src, m_idx, w1, d1, qs)
+    for i in (0, 1, 3):
+        e = m_idx[i]
+        y = (e4m3.decode(x[src[i]]) @ e4m3.decode(w1[e]).T) * float(d1[e])
+        g, u = y[:128], y[128:]
+        assert np.allclose(h[i], g / (1 + np.exp(-g)) * u, rtol=1e-13, atol=0)
+        assert np.array_equal(q[i], (h[i].astype(np.float32) * qs[e]).astype(np.float32))
+    assert np.all(np.isnan(h[2])) and np.all(np.isnan(q[2]))
+
+
+def test_per_tensor_fc2_reduces_to_the_groupwise_form_with_constant_scales():
+    rng = np.random.default_rng(71)
+    a2 = rng.integers(0, 0x7E, (256, 256)).astype(np.uint8)
+    w2 = rng.integers(0, 0x7E, (2, 384, 256)).astype(np.uint8)
+    d2 = np.array([0.3, 1.7], np.float32)
+    m_idx = np.array([0] * 128 + [1] * 100 + [-1] * 28)
+    got = moe.fc2_per_tensor(a2, m_idx, w2, d2)
+    sb = np.stack([np.full((3, 2), d, np.float32) for d in d2])
+    want = gemm_module.group_gemm_contiguous(a2, w2, np.ones((256, 2), np.float32), sb, m_idx)
+    np.testing.assert_allclose(got[m_idx >= 0], want[m_idx >= 0], rtol=1e-13)
+    assert np.all(np.isnan(got[m_idx < 0]))
+
+
+def test_combine_without_weights_sums_the_rows():
+    y2 = np.arange(12, dtype=np.float64).reshape(4, 3)
+    rows = np.array([[0, 3], [2, -1]])
+    assert np.array_equal(moe.combine(y2, rows, None), np.array([y2[0] + y2[3], y2[2]]))
+
+
+def test_per_tensor_chain_stage_identities():
+    rng = np.random.default_rng(72)
+    t, h_, e, k, i = 6, 256, 3, 2, 128
+    x = rng.integers(0, 0x7E, (t, h_)).astype(np.uint8)
+    ids = np.stack([rng.permutation(e)[:k] for _ in range(t)]).astype(np.int32)
+    w1 = rng.integers(0, 0x7E, (e, 2 * i, h_)).astype(np.uint8)
+    w2 = rng.integers(0, 0x7E, (e, h_, i)).astype(np.uint8)
+    d1 = np.full(e, 1e-3, np.float32)
+    qs = np.array([0.05], np.float32)
+    d2 = np.full(e, 0.01, np.float32)
+    r = moe.moe_ffn_per_tensor(x, ids, w1, w2, d1, qs, d2)
+    perm = r["perm"]
+    valid = perm["m_indices"] >= 0
+    assert np.array_equal(r["a2"][valid], moe.quantize_per_tensor(r["q"][valid]))
+    y2 = bf16.round_to_bf16(moe.fc2_per_tensor(r["a2"], perm["m_indices"], w2, d2))
+    assert np.array_equal(np.nan_to_num(r["y2"]), np.nan_to_num(y2))
+    assert np.array_equal(r["out"], moe.combine(np.nan_to_num(y2), perm["row_of_entry"], None))

@@ -15,6 +15,8 @@ Workloads (all seed-fixed):
   moe          router logits ~ N(0,1) (T,E); p = softmax; top-k by p (ties -> lower expert index);
                weights = p at the chosen experts (not renormalised); X ~ N(0,1) in BF16;
                W1 (E, 2I, H) and W2 (E, H, I) ~ N(0,1) quantised per 128x128 block.
+  moe (per-tensor)  x, W1, W2 ~ N(0,1) as E4M3 with one scale per tensor (per expert for the
+               weights); fixed activation scale 16 * hidden / 448.
   bmm          A (B,m,k), B (B,k,n) ~ N(0,1) quantised with amax/448 per row of A / per column of B
                (channelwise) or per tensor.
   norm         add-RMSNorm input ~ N(0,1), residual ~ N(0,1) times a per-row log-uniform scale,
@@ -145,6 +147,32 @@ def moe(num_tokens: int = 4096, hidden: int = 7168, num_experts: int = 64, top_k
     return dict(x=x, topk_ids=torch.from_numpy(ids).to(device), topk_weights=torch.from_numpy(w).to(device),
                 w1=w1, s1=s1, w2=w2, s2=s2, num_tokens=num_tokens, hidden=hidden,
                 num_experts=num_experts, top_k=top_k, inter=inter)
+
+
+def moe_per_tensor(num_tokens: int = 4096, hidden: int = 7168, num_experts: int = 64, top_k: int = 8,
+                   inter: int = 2048, seed: int = 0, device="cpu"):
+    """Per-tensor FP8 expert-FFN inputs: x ~ N(0,1) as E4M3 codes with one scale amax/448 over the
+    tensor, W1/W2 ~ N(0,1) with one scale per expert, the router of ``moe``. The dequantisation
+    scales are fc1_dequant[e] = s_x * s_w1[e] and fc2_dequant[e] = s_act * s_w2[e], with a fixed
+    activation scale s_act = 16 * hidden / 448 (h = silu(g) * u has a spread of about hidden for
+    unit-variance codes; larger values saturate) and fc2_quant = 1 / s_act."""
+    ids, w = router(num_tokens, num_experts, top_k, seed)
+    g = _gen(seed, device)
+
+    def quant(t, dims):
+        amax = t.abs().amax(dim=dims, keepdim=True)
+        scale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+        return (t / scale).to(torch.float8_e4m3fn).view(torch.uint8).contiguous(), scale.reshape(-1)
+
+    x, sx = quant(_normal((num_tokens, hidden), g, device), (0, 1))
+    w1, sw1 = quant(_normal((num_experts, 2 * inter, hidden), g, device), (1, 2))
+    w2, sw2 = quant(_normal((num_experts, hidden, inter), g, device), (1, 2))
+    s_act = 16.0 * hidden / E4M3_MAX
+    return dict(x=x, topk_ids=torch.from_numpy(ids).to(device), topk_weights=torch.from_numpy(w).to(device),
+                w1=w1, w2=w2, fc1_dequant=(sx * sw1).float().contiguous(),
+                fc2_quant=torch.tensor([1.0 / s_act], dtype=torch.float32, device=device),
+                fc2_dequant=(s_act * sw2).float().contiguous(), fc1_input_dequant=sx.float().contiguous(),
+                num_tokens=num_tokens, hidden=hidden, num_experts=num_experts, top_k=top_k, inter=inter)
 
 
 def bmm(batch: int, m: int, n: int, k: int, channel_a: bool, channel_b: bool, seed: int = 0, device="cpu"):
