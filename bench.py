@@ -13,8 +13,8 @@ the same workload.
 --configs adds the other workloads (contiguous grouped over 32 Zipf-sized experts, masked batched
 over 16 groups, the channelwise-scaled batched GEMM (8 x 1024x4096x7168, B transposed in the
 call), the add-RMSNorm + 1x128 quantiser and the plain quantiser over 4096x7168 BF16, the
-4096-token expert FFN with block scales and with per-tensor scales), each timed per launch with the caches evicted in between by a 512 MB read,
-under "configs". Two context lines are timed back to back like the headline: the per-tensor batched
+4096-token expert FFN with block scales and with per-tensor scales), each timed per launch with
+the caches evicted in between by a 512 MB read, under "configs". Two context lines are timed back to back like the headline: the per-tensor batched
 GEMM at batch 1 on the headline shape (the same matrix-core loop without per-block promotion), and
 hipBLASLt's per-tensor FP8 GEMM (torch._scaled_mm) on that shape, which is not this path.
 """
