@@ -15,7 +15,7 @@ import torch
 
 import moe_expert_matmul_amd as fp8g
 import workloads
-from oracle import bf16, moe as omoe, norm as onorm
+from oracle import bf16, e4m3, moe as omoe, norm as onorm
 from parity import host, say
 
 pytestmark = pytest.mark.gpu
@@ -44,6 +44,56 @@ def test_quantize_1x128_bit_exact(rows, cols, major):
     fp8g.fp8_quantize_1x128(x, out, sc, major)
     torch.cuda.synchronize()
     codes, scales = omoe.quantize_1x128(bf16.from_bf16_bits(host(x)).astype(np.float32))
+    assert np.array_equal(_scales_k_major(host(sc), major), scales)
+    assert np.array_equal(host(out), codes)
+
+
+def _near_midpoint_rows(seed=0):
+    """BF16 rows whose quotients x / (amax/448) fall on or within two FP32 ulps of a rounding midpoint
+    between E4M3 codes: the cases where a division off by one ulp would change the code. Each
+    128-wide block starts with its amax, followed by such x values for that amax."""
+    rng = np.random.default_rng(seed)
+    codes = np.arange(0x7F, dtype=np.uint8)
+    e4 = np.unique(e4m3.decode(codes))
+    mids = ((e4[1:] + e4[:-1]) / 2).astype(np.float32)
+    xs_bits = np.arange(1, 0x7F80, dtype=np.uint16)
+    xs = (xs_bits.astype(np.uint32) << 16).view(np.float32)
+    blocks = []
+    for ab in rng.integers(0x3000, 0x5000, 1500).astype(np.uint16):
+        amax = (np.array([ab], np.uint32) << 16).view(np.float32)[0]
+        s = np.float32(amax) / np.float32(448)
+        cand = xs_bits[xs <= amax]
+        q = (xs[xs <= amax] / s).astype(np.float32)
+        idx = np.clip(np.searchsorted(mids, q), 1, len(mids) - 1)
+        near = np.zeros(q.shape, bool)
+        for off in (0, -1):
+            near |= np.abs(q.view(np.int32) - mids[idx + off].view(np.int32)) <= 2
+        sel = cand[near][:127]
+        if sel.size == 0:
+            continue
+        blk = np.zeros(128, np.uint16)
+        blk[0] = ab
+        blk[1:1 + sel.size] = sel
+        signs = rng.random(128) < 0.5
+        blk[1:] ^= np.where(signs[1:], np.uint16(0x8000), np.uint16(0))
+        blocks.append(blk)
+    rows = len(blocks) // 8
+    return np.stack(blocks[:rows * 8]).reshape(rows, 8 * 128)
+
+
+@pytest.mark.parametrize("major", ["K", "MN"])
+def test_quantize_1x128_on_rounding_midpoints(major):
+    """Quotients on or next to the E4M3 rounding midpoints: bit for bit against the oracle's IEEE
+    float32 division, so the kernel's division must be correctly rounded there."""
+    bits = _near_midpoint_rows()
+    rows, cols = bits.shape
+    say("quantize_1x128 midpoints", rows, cols, major)
+    x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+    out = torch.empty((rows, cols), dtype=torch.uint8, device=DEV)
+    sc = torch.empty((rows, cols // 128) if major == "K" else (cols // 128, rows), dtype=torch.float32, device=DEV)
+    fp8g.fp8_quantize_1x128(x, out, sc, major)
+    torch.cuda.synchronize()
+    codes, scales = omoe.quantize_1x128(bf16.from_bf16_bits(bits).astype(np.float32))
     assert np.array_equal(_scales_k_major(host(sc), major), scales)
     assert np.array_equal(host(out), codes)
 
