@@ -28,6 +28,17 @@
 // drops tiles at or beyond masked_m[g]; the contiguous form reads the tile's 128 m_indices and drops
 // tiles that hold only padding. Rows that are not valid are still computed when they share a wave
 // with valid rows (each output row depends only on its own a row and scale) but never stored.
+//
+// Modes (the MODE template argument) on the same loop:
+//   PLAIN, CONTIG, MASKED  the three forms above; BF16 or FP16 out, and E4M3 with an output scale in
+//                          the plain form;
+//   CONTIG_SWIGLU          the expert FFN's fc1: SiLU(gate)*up and its 1x128 requantisation in the
+//                          epilogue (flashinfer-rs README, "API Example: Fused MoE FP8 (cudarc)");
+//   BMM                    bmm_fp8 of the MATE page: per-tensor or per-row/column scales, so each
+//                          MFMA accumulates straight into the sum over all of K and the scales are
+//                          applied once in the epilogue;
+//   CONTIG_PT(_SWIGLU)     the README's per-tensor FP8 FFN: the BMM loop under the contiguous
+//                          scheduler, one dequantisation scale per expert.
 #include "gemm_common.h"
 
 namespace fp8g {
