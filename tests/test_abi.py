@@ -167,3 +167,17 @@ def test_producers_validate_arguments(lib):
     st, msg = _status(f, P, P, P, P, Q, P, 1e-6, 4, 128, 3, None)
     assert st == _lib.INVALID_ARGUMENT and "scale_major" in msg
     assert f(None, None, None, None, None, None, 1e-6, 0, 7168, 0, None) == _lib.OK
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    # The package has no CPU fallback: without libfp8g.so the first call raises.
+    code = ("import moe_expert_matmul_amd as m, moe_expert_matmul_amd._lib as L\n"
+            f"L.LIB_PATH = {str(tmp_path / 'absent.so')!r}\n"
+            "try:\n    L.load()\nexcept ImportError as e:\n    print('raised', e)\n")
+    r = subprocess.run(["python3", "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert "raised" in r.stdout and "absent.so" in r.stdout
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run(["python3", os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr
