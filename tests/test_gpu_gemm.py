@@ -492,3 +492,31 @@ def test_contiguous_full_size_sampled():
     ref = _contig_ref(d, rows=rows, col_blocks=col_blocks)
     cols = np.concatenate([np.arange(c * 128, c * 128 + 128) for c in col_blocks])
     assert_within_tolerance(bf16_values(out)[rows][:, cols], ref, "contiguous full size sampled")
+
+
+@pytest.mark.parametrize("form", ["plain", "contiguous", "masked"])
+def test_repeated_launches_are_bitwise_identical(form):
+    """The pipeline synchronises LDS stages with a fence-free barrier and counted waits on the LDS
+    DMA loads; a missing wait would show up as launches that disagree. 40 back-to-back launches of
+    each form at a multi-wave size must give the same bytes."""
+    say("repeated launches", form)
+    if form == "plain":
+        d = workloads.plain(2048, 2048, 2048, seed=31, device=DEV)
+        out = torch.empty((2048, 2048), dtype=torch.bfloat16, device=DEV)
+        run = lambda: fp8g.fp8_gemm_nt_groupwise(d["a"], d["b"], d["a_scale"], d["b_scale"], out)
+    elif form == "contiguous":
+        d = workloads.contiguous(8, n=1024, k=2048, seed=32, device=DEV, counts=[300, 700, 0, 129, 800, 64, 200, 500])
+        out = torch.zeros((d["m"], 1024), dtype=torch.bfloat16, device=DEV)
+        run = lambda: fp8g.fp8_group_gemm_contiguous(d["a"], d["b"], d["a_scale"], d["b_scale"], d["m_indices"], out)
+    else:
+        d = workloads.masked(8, 256, 1024, 2048, 128, seed=33, device=DEV,
+                             masked_m=np.array([256, 1, 130, 0, 200, 64, 255, 128], np.int32))
+        out = torch.zeros((8, 256, 1024), dtype=torch.bfloat16, device=DEV)
+        run = lambda: fp8g.fp8_batch_gemm_masked(d["a"], d["b"], d["a_scale"], d["b_scale"], d["masked_m"], 128, out)
+    run()
+    torch.cuda.synchronize()
+    first = out.clone()
+    for _ in range(40):
+        run()
+        assert torch.equal(out, first), f"{form}: a repeated launch changed the output"
+    torch.cuda.synchronize()
