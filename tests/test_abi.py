@@ -181,3 +181,16 @@ def test_missing_library_fails_loudly(tmp_path):
 def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run(["python3", os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_header_and_library_work_from_plain_c(tmp_path):
+    """The boundary is a C ABI: a C program compiled against include/fp8g.h and linked with
+    libfp8g.so validates arguments and reports errors without Python."""
+    exe = tmp_path / "abi_from_c"
+    lib_dir = os.path.dirname(_lib.LIB_PATH)
+    build = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                            os.path.join(ROOT, "tests", "c", "abi_from_c.c"), "-L", lib_dir, "-lfp8g",
+                            f"-Wl,-rpath,{lib_dir}", "-o", str(exe)], capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert run.returncode == 0 and run.stdout.strip() == "ok", (run.returncode, run.stdout, run.stderr)
