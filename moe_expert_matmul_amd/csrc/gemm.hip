@@ -44,9 +44,11 @@
 namespace fp8g {
 namespace kernels {
 
-// The next stage's loads are issued over the first LOAD_GROUPS column groups of a K block, and
-// each column group reads the b fragment of the group BPRE ahead of it.
+// The next stage's loads are issued over the first LOAD_GROUPS column groups of a K block (the
+// first LOAD_GROUPS_DEFER in the deferred schedule of the plain and masked forms), and each column
+// group reads the b fragment of the group BPRE ahead of it.
 constexpr int LOAD_GROUPS = 4;
+constexpr int LOAD_GROUPS_DEFER = 6;
 constexpr int BPRE = 2;
 
 template <int BM, int BN, int WM, int WN, int STAGES>
@@ -455,6 +457,111 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
       for (int r = 0; r < 4; ++r) acc[ig][T::JG - 1][r] = __builtin_fmaf(prod[T::JG - 1][ig][r], s_up[ig], acc[ig][T::JG - 1][r]);
   };
 
+  // Deferred schedule (plain and masked forms): the MFMAs of the last column group of block kb-1,
+  // and the promotions of its last two groups, run after the barrier that opens block kb,
+  // interleaved with the reads of block kb's a fragments, so the matrix core has work while those
+  // reads are in flight. Their operands are already in registers, so the stage they came from may
+  // be refilled. The products and every FP32 operation are those of `compute`, in the same order
+  // per output: the results are identical. (The contiguous form's 256-row tiles would spill
+  // registers with it, so the grouped forms keep `compute`.)
+  constexpr bool DEFER = !NO_PROMOTION && (MODE == MODE_PLAIN || MODE == MODE_MASKED);
+  constexpr int LGD = (T::JG - 1) < LOAD_GROUPS_DEFER ? (T::JG - 1) : LOAD_GROUPS_DEFER;
+  constexpr auto load_first_d = [](int jg) { return ((jg < LGD ? jg : LGD) * T::LOADS + LGD - 1) / LGD; };
+  static_assert(!DEFER || (T::JG >= 3 && BPRE < T::JG), "the deferred schedule needs three column groups");
+  i32x8 dq_a[T::IG];
+  i32x8 dq_b[T::JG];
+  f32x4 dq_prod[T::JG][T::IG];
+  float dq_s[T::IG];   // sa*sb of the block being computed
+  float dq_sp[T::IG];  // sa*sb of the previous block, for its deferred promotions
+
+  auto compute_deferred = [&](int kb, int kb_load, bool load_live, bool first) {
+    const uint8_t* sA = smem + (kb % STAGES) * T::STAGE_BYTES;
+    const uint8_t* sB = sA + T::A_BYTES;
+    const float* sSA = reinterpret_cast<const float*>(sA + T::SA_OFF);
+    const float* sSB = reinterpret_cast<const float*>(sA + T::SB_OFF);
+#pragma unroll
+    for (int ig = 0; ig < T::IG; ++ig) dq_sp[ig] = dq_s[ig];
+    const float sbv = sSB[(col0 + j0) / 128 - col0 / 128];
+#pragma unroll
+    for (int ig = 0; ig < T::IG; ++ig) dq_s[ig] = sSA[i0 + ig * 16 + fr] * sbv;
+    dq_b[0] = load_frag(sB, j0 + fr, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!first) {
+      // block kb-1: last group's MFMAs, the promotions of its second-to-last group, and this
+      // block's a fragments read into the registers each MFMA has just consumed
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int ig = 0; ig < T::IG; ++ig) {
+        dq_prod[T::JG - 1][ig] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            dq_b[T::JG - 1], dq_a[ig], f32x4{0.f, 0.f, 0.f, 0.f}, FMT_E4M3, FMT_E4M3, 0, E8M0_ONE, 0, E8M0_ONE);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc[ig][T::JG - 2][r] = __builtin_fmaf(dq_prod[T::JG - 2][ig][r], dq_sp[ig], acc[ig][T::JG - 2][r]);
+        dq_a[ig] = load_frag(sA, i0 + ig * 16 + fr, lane);
+      }
+#pragma unroll
+      for (int ig = 0; ig < T::IG; ++ig) {
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_VALU, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+    } else {
+#pragma unroll
+      for (int ig = 0; ig < T::IG; ++ig) dq_a[ig] = load_frag(sA, i0 + ig * 16 + fr, lane);
+    }
+#pragma unroll
+    for (int jg = 1; jg < BPRE; ++jg) dq_b[jg] = load_frag(sB, j0 + jg * 16 + fr, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    // groups 0 .. JG-2 of block kb; group 0's MFMAs carry the last promotions of block kb-1
+#pragma unroll
+    for (int jg = 0; jg < T::JG - 1; ++jg) {
+#pragma unroll
+      for (int i = load_first_d(jg); i < load_first_d(jg + 1); ++i) issue_load(kb_load, i, load_live);
+      if (jg + BPRE < T::JG) dq_b[jg + BPRE] = load_frag(sB, j0 + (jg + BPRE) * 16 + fr, lane);
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int ig = 0; ig < T::IG; ++ig) {
+        dq_prod[jg][ig] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            dq_b[jg], dq_a[ig], f32x4{0.f, 0.f, 0.f, 0.f}, FMT_E4M3, FMT_E4M3, 0, E8M0_ONE, 0, E8M0_ONE);
+        if (jg > 0) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[ig][jg - 1][r] = __builtin_fmaf(dq_prod[jg - 1][ig][r], dq_s[ig], acc[ig][jg - 1][r]);
+        } else if (!first) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[ig][T::JG - 1][r] = __builtin_fmaf(dq_prod[T::JG - 1][ig][r], dq_sp[ig], acc[ig][T::JG - 1][r]);
+        }
+      }
+      sched_vmem_group(load_first_d(jg + 1) - load_first_d(jg));
+      if (jg + BPRE < T::JG) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+#pragma unroll
+      for (int ig = 0; ig < T::IG; ++ig) {
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+        if (jg > 0 || !first) __builtin_amdgcn_sched_group_barrier(SG_VALU, 4, 0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // what the last block left deferred: its last group's MFMAs and its last two promotions
+  auto compute_deferred_tail = [&]() {
+#pragma unroll
+    for (int ig = 0; ig < T::IG; ++ig) {
+      dq_prod[T::JG - 1][ig] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          dq_b[T::JG - 1], dq_a[ig], f32x4{0.f, 0.f, 0.f, 0.f}, FMT_E4M3, FMT_E4M3, 0, E8M0_ONE, 0, E8M0_ONE);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        acc[ig][T::JG - 2][r] = __builtin_fmaf(dq_prod[T::JG - 2][ig][r], dq_s[ig], acc[ig][T::JG - 2][r]);
+    }
+#pragma unroll
+    for (int ig = 0; ig < T::IG; ++ig)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        acc[ig][T::JG - 1][r] = __builtin_fmaf(dq_prod[T::JG - 1][ig][r], dq_s[ig], acc[ig][T::JG - 1][r]);
+  };
+
   // Pipeline: K block kb (slabs and scales) lives in stage kb % STAGES. Iteration kb waits until
   // its own loads, issued STAGES-1 iterations earlier, have landed -- with three stages the loads of
   // kb+1 stay in flight -- synchronises the workgroup (which also retires every read of the stage
@@ -465,6 +572,8 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   for (int ig = 0; ig < T::IG; ++ig)
 #pragma unroll
     for (int jg = 0; jg < T::JG; ++jg) acc[ig][jg] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ig = 0; ig < T::IG; ++ig) dq_s[ig] = 0.0f;
   if (KB > 0) {
 #pragma unroll
     for (int b = 0; b < STAGES - 1; ++b) issue_loads(b, b < KB);
@@ -478,10 +587,18 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     if (wave_live) {
       if constexpr (NO_PROMOTION)
         compute_bmm(kb, kb_load, kb_load < KB);
-      else
+      else if constexpr (DEFER) {
+        if (kb == 0)
+          compute_deferred(kb, kb_load, kb_load < KB, true);
+        else
+          compute_deferred(kb, kb_load, kb_load < KB, false);
+      } else
         compute(kb, kb_load, kb_load < KB);
     } else
       issue_loads(kb_load, kb_load < KB);
+  }
+  if constexpr (DEFER) {
+    if (wave_live && KB > 0) compute_deferred_tail();
   }
   wait_vmcnt<0>();  // the zero-fill loads of the last iterations
 
