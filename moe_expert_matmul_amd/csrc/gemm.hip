@@ -22,6 +22,10 @@
 // LDS's full rate. The swizzle is applied on the global side: lane l of a load writes LDS chunk l of
 // its 1 KB slab and fetches the logical chunk that belongs there.
 //
+// In the plain and masked forms the MFMAs of a K block's last column group (and the promotions of
+// its last two groups) are issued after the barrier that opens the next block, while that block's
+// first fragment reads are in flight; each output still receives its promotions in K-block order.
+//
 // Tile scheduling: the 1-D grid is renumbered so that consecutive tiles run on the same XCD (the
 // hardware deals workgroups round-robin over the 8 XCDs, each with its own L2) and then rasterised
 // in groups of `group_m` row tiles. The masked form maps the grid to (group, row tile, col tile) and

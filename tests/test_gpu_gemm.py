@@ -331,6 +331,19 @@ def test_masked_matches_oracle_and_leaves_other_rows(expected_m):
         assert not keep[g, :mm[g]].any()
 
 
+@pytest.mark.parametrize("k", [128, 256])
+def test_masked_short_k_matches_oracle(k):
+    """One and two K blocks: the masked form's schedule carries each block's last column group
+    into the next block, so these cover a loop that is all first block and tail."""
+    G, max_m, n = 3, 256, 384
+    mm = np.array([256, 70, 129], np.int32)
+    say("masked short k", G, max_m, n, k, mm.tolist())
+    for expected_m in (32, 256):  # 128- and 256-row tiles
+        d = workloads.masked(G, max_m, n, k, expected_m, seed=11 + k, device=DEV, masked_m=mm)
+        out = _masked_call(d)
+        assert_within_tolerance(bf16_values(out), _masked_ref(d, mm), f"masked k={k} expected_m={expected_m}")
+
+
 def test_masked_expected_m_never_changes_results():
     G, max_m, n, k = 3, 256, 256, 384
     mm = np.array([256, 100, 3], np.int32)
