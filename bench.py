@@ -13,8 +13,10 @@ the same workload.
 --configs adds the other workloads (contiguous grouped over 32 Zipf-sized experts, masked batched
 over 16 groups, the channelwise-scaled batched GEMM (8 x 1024x4096x7168, B transposed in the
 call), the add-RMSNorm + 1x128 quantiser and the plain quantiser over 4096x7168 BF16, the
-4096-token expert FFN with block scales and with per-tensor scales), each timed per launch with
-the caches evicted in between by a 512 MB read, under "configs". Two context lines are timed back to back like the headline: the per-tensor batched
+4096-token expert FFN with block scales and with per-tensor scales, and one GPU's share of the
+block-scale FFN under 8-way expert parallelism: 8 of the 64 experts), each timed per launch with
+the caches evicted in between by a 512 MB read, under "configs". Two context lines are timed back
+to back like the headline: the per-tensor batched
 GEMM at batch 1 on the headline shape (the same matrix-core loop without per-block promotion), and
 hipBLASLt's per-tensor FP8 GEMM (torch._scaled_mm) on that shape, which is not this path.
 """
@@ -226,6 +228,21 @@ def other_configs(steps, warmup):
     res["moe_ffn_4096tok_h7168_e64_top8_i2048"] = {
         "ms": round(med, 4), "ms_best": round(best, 4), "tflops": round(flops / med / 1e9, 2),
         "frac_mfma": round(flops / med / 1e9 / FP8_DENSE_PEAK_TFLOPS, 4)}
+
+    # One GPU's share under 8-way expert parallelism: experts 0-7 of the same 64 and every token's
+    # routes; routes to other experts fall outside [0, 8) and are left to the other GPUs, so the
+    # output is this GPU's partial sum (the part an all-to-all would return).
+    shard = 8
+    ws = fp8g.MoeWorkspace.allocate(4096, 8, shard, 7168, 2048, dev)
+    fn = lambda: fp8g.moe_ffn_fp8_block_scale(d["x"], d["topk_ids"], d["topk_weights"], d["w1"][:shard],
+                                              d["s1"][:shard], d["w2"][:shard], d["s2"][:shard], out=out,
+                                              workspace=ws)
+    med, best = time_cold(fn, steps, warmup, flush)
+    rows = int((d["topk_ids"] < shard).sum().item())
+    flops = 2.0 * rows * 4096 * 7168 + 2.0 * rows * 7168 * 2048
+    res["moe_ffn_ep8_shard_8of64experts_4096tok_h7168_top8_i2048"] = {
+        "ms": round(med, 4), "ms_best": round(best, 4), "tflops": round(flops / med / 1e9, 2),
+        "frac_mfma": round(flops / med / 1e9 / FP8_DENSE_PEAK_TFLOPS, 4), "local_rows": rows}
     del d, ws, out
 
     d = workloads.moe_per_tensor(seed=0, device=dev)
@@ -235,6 +252,8 @@ def other_configs(steps, warmup):
                                              d["fc2_quant"], d["fc2_dequant"], d["fc1_input_dequant"], out=out,
                                              workspace=ws)
     med, best = time_cold(fn, steps, warmup, flush)
+    rows = 4096 * 8
+    flops = 2.0 * rows * 4096 * 7168 + 2.0 * rows * 7168 * 2048
     res["moe_ffn_per_tensor_4096tok_h7168_e64_top8_i2048"] = {
         "ms": round(med, 4), "ms_best": round(best, 4), "tflops": round(flops / med / 1e9, 2),
         "frac_mfma": round(flops / med / 1e9 / FP8_DENSE_PEAK_TFLOPS, 4)}

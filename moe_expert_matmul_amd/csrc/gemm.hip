@@ -215,13 +215,19 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     t -= g * per;
   }
   int tm, tn;
-  raster(t, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-  // Contiguous form with 256-row tiles: the grid holds two entries per row tile (tm = 2 * tile +
-  // half), so a tile whose two 128-row halves belong to different experts runs as two workgroups.
+  // Contiguous form with 256-row tiles: the grid holds two entries per tile and column tile (one
+  // per 128-row half), so a tile whose halves belong to different experts runs as two workgroups.
+  // Its tile rows are dealt round-robin over the XCDs, each with all its entries (so they share
+  // the tile's a rows in one L2): the live rows of an expert workspace sized for the worst case
+  // are a prefix of it, and this spreads any prefix over every XCD.
   int half = 0;
   if (CONTIG && BM == 256) {
-    half = tm & 1;
-    tm >>= 1;
+    int k;
+    xcd_row_interleave(blockIdx.x, p.tiles_m / 2, 2 * p.tiles_n, tm, k);
+    half = k / p.tiles_n;
+    tn = k - half * p.tiles_n;
+  } else {
+    raster(t, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
   }
   const int row0 = tm * BM;
   const int col0 = tn * BN;

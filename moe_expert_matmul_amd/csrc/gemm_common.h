@@ -92,6 +92,25 @@ __device__ __forceinline__ int xcd_local_order(int t, int total) {
   return t < full ? (t & 7) * (full >> 3) + (t >> 3) : t;
 }
 
+// Row r of `rows` rows, each with `per_row` consecutive entries, for workgroup id b: XCD x (ids
+// with b % 8 == x) receives rows x, x+8, x+16, ... in order, each row's entries one after another;
+// the last rows % 8 rows follow in plain order. A bijection of [0, rows * per_row).
+__device__ __forceinline__ void xcd_row_interleave(int b, int rows, int per_row, int& row, int& entry) {
+  const int rem = rows & 7;
+  const int full = (rows - rem) * per_row;
+  if (b < full) {
+    const int j = b >> 3;
+    const int r = j / per_row;
+    entry = j - r * per_row;
+    row = r * 8 + (b & 7);
+  } else {
+    const int t = b - full;
+    const int r = t / per_row;
+    entry = t - r * per_row;
+    row = rows - rem + r;
+  }
+}
+
 __device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int group_m, int& tm, int& tn) {
   const int per_group = group_m * tiles_n;
   const int gid = t / per_group;

@@ -103,6 +103,37 @@ def _stagewise(d, out, ws, p, rows, token_sample, col_blocks_fc1, col_blocks_fc2
     return flips
 
 
+def test_moe_expert_parallel_shard_sampled():
+    """One GPU's share under 8-way expert parallelism, as bench.py times it: experts 0-7 of the
+    full-size workload with every token's routes; routes to experts 8-63 fall outside the shard and
+    are not computed, so each token's output is the sum over its local routes only (zero when it
+    has none)."""
+    say("moe expert-parallel shard: experts 0-7 of 64, T=4096 H=7168 k=8 I=2048")
+    d = dict(workloads.moe(seed=0, device=DEV))
+    shard = 8
+    for key in ("w1", "s1", "w2", "s2"):
+        d[key] = d[key][:shard]
+    d["num_experts"] = shard
+    out, ws = _run(d)
+    p = _check_permutation(d, ws)
+    mi = p["m_indices"]
+    ids = host(d["topk_ids"])
+    assert int((mi >= 0).sum()) == int((ids < shard).sum())
+    rng = np.random.default_rng(5)
+    rows = []
+    for e in (0, 3, 7):
+        r = np.nonzero(mi == e)[0]
+        rows += [r[0], r[-1]]
+    rows += rng.choice(np.nonzero(mi >= 0)[0], 6, replace=False).tolist()
+    rows = np.unique(np.array(rows))
+    remote_only = np.nonzero((ids >= shard).all(axis=1))[0]
+    assert remote_only.size > 0
+    tokens = np.unique(np.concatenate([[0, 4095], remote_only[:3], rng.choice(4096, 11, replace=False)]))
+    flips = _stagewise(d, out, ws, p, rows, tokens, [0, 16, 31], [0, 27, 55])
+    assert not bf16_values(out)[remote_only].any(), "tokens with no local route must come out zero"
+    say("requant code flips on sampled rows", flips)
+
+
 @pytest.mark.parametrize("num_tokens,top_k,num_experts", [(1, 1, 1), (5, 3, 7), (777, 1, 1024), (4096, 8, 64),
                                                             (20000, 6, 129)])
 def test_permutation_matches_oracle(num_tokens, top_k, num_experts):
