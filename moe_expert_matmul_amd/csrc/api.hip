@@ -304,10 +304,10 @@ void group_gemm_contiguous(const void* a, const float* a_scale, int64_t a_src_ro
   // counts two entries per 256-row tile.
   // Short K with large expert regions (the expert FFN's fc2: k = 2048, about 600 rows per expert):
   // a K loop of 16 blocks pays a tile's prologue and epilogue often, and 256x256 tiles halve their
-  // number (measured 796 against 854 us at the 4096-token FFN workload with block scales; no gain
-  // with per-tensor scales or in fc1).
-  fp8g::TileConfig cfg = (!pt && !swiglu && k <= 2048 && m >= 512 * num_groups) ? fp8g::TILE_256x256
-                                                                                 : fp8g::TILE_128x256;
+  // number (measured at the 4096-token FFN workload: 796 against 854 us with block scales, 723
+  // against 789 us with per-tensor scales; fc1 gains nothing from them).
+  fp8g::TileConfig cfg = (!swiglu && k <= 2048 && m >= 512 * num_groups) ? fp8g::TILE_256x256
+                                                                         : fp8g::TILE_128x256;
   if (fp8g::tile_override() >= 0) cfg = (fp8g::TileConfig)fp8g::tile_override();
   if (swiglu && fp8g::tile_cols(cfg) != 256) cfg = fp8g::TILE_128x256;  // gate and up share a 256-wide tile
   p.tiles_m = (int32_t)(ceil_div(m, fp8g::tile_rows(cfg)) * (fp8g::tile_rows(cfg) / 128));
