@@ -240,6 +240,17 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   // covers its own half (or exits when that half is padding only).
   int bsel = 0;
   int half_mask = 3;
+  // Contiguous form: the tile's m_indices, one entry per lane and 64-row quarter, all loaded before
+  // any is used so the tile's head costs one memory round trip (m is a multiple of 128, so a half
+  // whose first row is in range lies wholly in range).
+  constexpr int QUARTERS = CONTIG ? BM / 64 : 1;
+  int tile_ids[QUARTERS];
+  // Tile row of this lane's a load q (q < A_LOADS) and of its a-scale load (q == A_LOADS), clamped
+  // to the valid rows; with gathered rows (a_rows), their indices are loaded with the m_indices.
+  auto a_tile_row = [&](int q, int last) {
+    return min(q < T::A_LOADS ? row0 + (wave * T::A_LOADS + q) * SLAB_ROWS + (lane >> 3) : row0 + wave * 64 + lane, last);
+  };
+  int gathered[T::A_LOADS + 1];
   if (MODE == MODE_BMM) {
     bsel = g;
   } else if (MODE == MODE_MASKED) {
@@ -249,14 +260,18 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     bsel = g;
   } else if (CONTIG) {
     constexpr int HALVES = BM / 128;
+#pragma unroll
+    for (int q = 0; q < QUARTERS; ++q)
+      tile_ids[q] = row0 + (q / 2) * 128 < p.m ? p.rowinfo[row0 + q * 64 + lane] : -1;
+    if (p.a_rows != nullptr) {
+#pragma unroll
+      for (int q = 0; q <= T::A_LOADS; ++q) gathered[q] = p.a_rows[a_tile_row(q, p.m - 1)];
+    }
     int ex[HALVES];
 #pragma unroll
     for (int h = 0; h < HALVES; ++h) {
-      int e = -1;
-      if (row0 + h * 128 < p.m)
-        for (int r = lane; r < 128; r += 64) e = max(e, p.rowinfo[row0 + h * 128 + r]);
-      e = __builtin_amdgcn_readfirstlane(wave_max(e));  // uniform: keeps b's resource scalar
-      ex[h] = (e >= 0 && e < p.num_groups) ? e : -1;       // -1: padding only
+      const int e = __builtin_amdgcn_readfirstlane(wave_max(max(tile_ids[2 * h], tile_ids[2 * h + 1])));  // uniform: keeps b's resource scalar
+      ex[h] = (e >= 0 && e < p.num_groups) ? e : -1;  // -1: padding only
     }
     if (HALVES == 2 && ex[0] >= 0 && ex[0] == ex[HALVES - 1]) {
       if (half == 1) return;
@@ -283,20 +298,24 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     const int q = v / (2 * OUTW), r = v % (2 * OUTW);
     return (r < OUTW ? 0 : p.inter) + 128 * tn + q * OUTW + (r % OUTW);
   };
-  // The row of a (and of a_scale) that tile row r reads: r itself, or a_rows[r] when the contiguous
-  // form gathers its rows (rows whose index is out of range read row 0; they are never stored).
-  auto a_source_row = [&](int r) {
-    if (!CONTIG || p.a_rows == nullptr) return r;
-    const int s = p.a_rows[r];
-    return (s >= 0 && s < p.a_src_rows) ? s : 0;
-  };
+  // The rows of a this lane's a loads read (entries 0 .. A_LOADS-1) and the row of a_scale its
+  // scale load reads (entry A_LOADS, used by the a-scale waves): the tile rows themselves, or
+  // a_rows[tile row] when the contiguous form gathers its rows (indices out of range read row 0;
+  // those rows are never stored).
+  int a_src[T::A_LOADS + 1];
+#pragma unroll
+  for (int q = 0; q <= T::A_LOADS; ++q) a_src[q] = a_tile_row(q, q < T::A_LOADS ? a_last : p.m - 1);
+  if (CONTIG && p.a_rows != nullptr) {
+#pragma unroll
+    for (int q = 0; q <= T::A_LOADS; ++q)
+      a_src[q] = (gathered[q] >= 0 && gathered[q] < p.a_src_rows) ? gathered[q] : 0;
+  }
   uint32_t a_off[T::A_LOADS], b_off[T::B_LOADS];
 #pragma unroll
   for (int q = 0; q < T::A_LOADS; ++q) {
     const int slab_row = (wave * T::A_LOADS + q) * SLAB_ROWS;
     const int lchunk = (lane & 7) ^ swizzle(slab_row + lrow);
-    const int r = a_source_row(min(row0 + slab_row + lrow, a_last));
-    a_off[q] = (uint32_t)r * (uint32_t)p.k + lchunk * 16;
+    a_off[q] = (uint32_t)a_src[q] * (uint32_t)p.k + lchunk * 16;
   }
 #pragma unroll
   for (int q = 0; q < T::B_LOADS; ++q) {
@@ -319,8 +338,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   uint32_t s_voff;
   int s_dst;
   if (a_scale_wave) {
-    const int r = a_source_row(min(row0 + wave * 64 + lane, p.m - 1));
-    s_voff = (uint32_t)r * p.sa_row_stride * 4;
+    s_voff = (uint32_t)a_src[T::A_LOADS] * p.sa_row_stride * 4;
     s_dst = T::SA_OFF + wave * 256;
   } else {
     const int nb = SWIGLU ? min((lane == 0 ? 0 : p.inter / 128) + tn, p.nblocks - 1)
@@ -344,7 +362,11 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   // other half's rows) only: one m_indices entry per lane, WTM == 64.
   if (CONTIG) {
     static_assert(T::WTM == 64, "one lane per wave row");
-    wave_live = wave_live && __ballot(p.rowinfo[row0 + i0 + lane] == bsel) != 0;
+    int mine = tile_ids[0];
+#pragma unroll
+    for (int q = 1; q < QUARTERS; ++q)
+      if (i0 == q * 64) mine = tile_ids[q];
+    wave_live = wave_live && __ballot(mine == bsel) != 0;
   }
 
   f32x4 acc[T::IG][T::JG];
