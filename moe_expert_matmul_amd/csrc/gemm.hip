@@ -95,7 +95,7 @@ constexpr float kE4M3MaxOut = 448.0f;  // largest finite E4M3FN value
 template <typename T, int WN>
 __device__ __forceinline__ void swiglu_epilogue(const GemmParams& p, const f32x4 (&acc)[T::IG][T::JG], uint8_t* smem,
                                                 int row0, int row_end, int bsel, int tn, int i0, int wave, int lane,
-                                                bool wave_live) {
+                                                bool wave_live, int wave_ids) {
   constexpr int OUTW = 128 / WN;
   constexpr int HALF = T::JG / 2;  // column groups of gate (then the same number of up)
   const int fr = lane & 15, q = wave % WN;
@@ -127,11 +127,14 @@ __device__ __forceinline__ void swiglu_epilogue(const GemmParams& p, const f32x4
   if (!wave_live) return;
   const int nblk = p.inter / 128;
   const int cl = (lane >> 4) * 4;
+  int row_id[T::IG];  // m_indices of each lane's rows, from the wave's registers
+#pragma unroll
+  for (int ig = 0; ig < T::IG; ++ig) row_id[ig] = __shfl(wave_ids, ig * 16 + fr, 64);
 #pragma unroll
   for (int ig = 0; ig < T::IG; ++ig) {
     const int tr = i0 + ig * 16 + fr;  // tile row
     const int i = row0 + tr;
-    if (i >= row_end || p.rowinfo[i] != bsel) continue;
+    if (i >= row_end || row_id[ig] != bsel) continue;
     float amax = 0.0f;
 #pragma unroll
     for (int w = 0; w < WN; ++w) amax = fmaxf(amax, amax_lds[w * 256 + tr]);
@@ -151,24 +154,25 @@ __device__ __forceinline__ void swiglu_epilogue(const GemmParams& p, const f32x4
 }
 
 // Epilogue of the per-tensor expert FFN's fc1 (CONTIG_PT_SWIGLU): gate and up are the FP32 sums
-// times the expert's dequantisation scale, h = silu(gate) * up in FP32 (silu(g) = g / (1 + exp(-g))),
+// times the expert's dequantisation scale d, h = silu(gate) * up in FP32 (silu(g) = g / (1 + exp(-g))),
 // and the code is E4M3_RNE(saturate(h * act_quant)) -- one per-tensor (or per-expert) scale, so no
 // row maximum and no exchange between waves. Column mapping as in swiglu_epilogue.
 template <typename T, int WN>
 __device__ __forceinline__ void swiglu_pt_epilogue(const GemmParams& p, const f32x4 (&acc)[T::IG][T::JG], int row0,
                                                    int row_end, int bsel, int tn, int i0, int wave, int lane,
-                                                   bool wave_live) {
+                                                   bool wave_live, int wave_ids, float d, float qs) {
   if (!wave_live) return;
   constexpr int OUTW = 128 / WN;
   constexpr int HALF = T::JG / 2;
   const int fr = lane & 15, q = wave % WN;
   const int cl = (lane >> 4) * 4;
-  const float d = p.group_dequant[bsel];
-  const float qs = p.act_quant[p.act_quant_per_group ? bsel : 0];
+  int row_id[T::IG];  // m_indices of each lane's rows, from the wave's registers
+#pragma unroll
+  for (int ig = 0; ig < T::IG; ++ig) row_id[ig] = __shfl(wave_ids, ig * 16 + fr, 64);
 #pragma unroll
   for (int ig = 0; ig < T::IG; ++ig) {
     const int i = row0 + i0 + ig * 16 + fr;
-    if (i >= row_end || p.rowinfo[i] != bsel) continue;
+    if (i >= row_end || row_id[ig] != bsel) continue;
     uint8_t* orow = p.q_out + (int64_t)i * p.inter + 128 * tn + q * OUTW;
 #pragma unroll
     for (int jg = 0; jg < HALF; ++jg) {
@@ -285,6 +289,14 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
 
   const uint8_t* A = p.a + (int64_t)g * p.a_group_stride;
   const float* SA = p.sa + (int64_t)g * p.sa_group_stride;
+  // Per-tensor modes: the expert's scales, and the plain form's E4M3 output scale, read now so that
+  // the epilogue waits on no load.
+  float pt_dequant = 1.0f, pt_act_quant = 1.0f, out_scale = 1.0f;
+  if (MODE == MODE_PLAIN && p.out_scale != nullptr) out_scale = *p.out_scale;
+  if constexpr (PT) {
+    pt_dequant = p.group_dequant[bsel];
+    if constexpr (MODE == MODE_CONTIG_PT_SWIGLU) pt_act_quant = p.act_quant[p.act_quant_per_group ? bsel : 0];
+  }
 
   // ---- HBM -> LDS load assignment ----------------------------------------------------------
   // Slab s (1 KB) holds tile rows [8s, 8s+8); lane l fills its chunk l, i.e. tile row
@@ -360,13 +372,16 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   bool wave_live = (row0 + i0 < row_end) && (col0 + j0 < p.n) && ((half_mask >> (i0 / 128)) & 1);
   // In the contiguous form a wave none of whose rows belongs to the expert holds padding (or the
   // other half's rows) only: one m_indices entry per lane, WTM == 64.
+  // wave_ids: lane l holds the m_indices entry of this wave's row i0 + l (the epilogue reads its
+  // rows' entries from here rather than from memory).
+  int wave_ids = -1;
   if (CONTIG) {
     static_assert(T::WTM == 64, "one lane per wave row");
-    int mine = tile_ids[0];
+    wave_ids = tile_ids[0];
 #pragma unroll
     for (int q = 1; q < QUARTERS; ++q)
-      if (i0 == q * 64) mine = tile_ids[q];
-    wave_live = wave_live && __ballot(mine == bsel) != 0;
+      if (i0 == q * 64) wave_ids = tile_ids[q];
+    wave_live = wave_live && __ballot(wave_ids == bsel) != 0;
   }
 
   f32x4 acc[T::IG][T::JG];
@@ -635,10 +650,11 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   wait_vmcnt<0>();  // the zero-fill loads of the last iterations
 
   if constexpr (MODE == MODE_CONTIG_PT_SWIGLU) {
-    swiglu_pt_epilogue<T, WN>(p, acc, row0, row_end, bsel, tn, i0, wave, lane, wave_live);
+    swiglu_pt_epilogue<T, WN>(p, acc, row0, row_end, bsel, tn, i0, wave, lane, wave_live, wave_ids, pt_dequant,
+                              pt_act_quant);
     return;
   } else if constexpr (SWIGLU) {
-    swiglu_epilogue<T, WN>(p, acc, smem, row0, row_end, bsel, tn, i0, wave, lane, wave_live);
+    swiglu_epilogue<T, WN>(p, acc, smem, row0, row_end, bsel, tn, i0, wave, lane, wave_live, wave_ids);
     return;
   }
 
@@ -650,7 +666,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   const int jl = (lane >> 4) * 4;
   const bool vec = (p.n & 3) == 0;
   if constexpr (MODE == MODE_CONTIG_PT) {
-    const float d = p.group_dequant[bsel];
+    const float d = pt_dequant;
 #pragma unroll
     for (int ig = 0; ig < T::IG; ++ig)
 #pragma unroll
@@ -677,8 +693,31 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     }
   }
   if (MODE == MODE_PLAIN && p.out_scale != nullptr) {
-    const float so = *p.out_scale;
+    const float so = out_scale;
     uint8_t* O = reinterpret_cast<uint8_t*>(p.out);
+    auto codes4 = [&](const f32x4& a) {
+      float q[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        q[r] = __fdiv_rn(a[r], so);
+        if (!(fabsf(q[r]) <= kE4M3MaxOut) && q[r] == q[r]) q[r] = copysignf(kE4M3MaxOut, q[r]);  // saturate; NaN stays
+      }
+      const int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+      return __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w, true);
+    };
+    if (vec && col0 + j0 + T::WTN <= p.n) {
+      // all of the wave's columns in range: row addresses formed once, stores at immediate offsets
+      int* rowp[T::IG];
+#pragma unroll
+      for (int ig = 0; ig < T::IG; ++ig)
+        rowp[ig] = reinterpret_cast<int*>(O + (int64_t)(row0 + i0 + ig * 16 + fr) * p.n + col0 + j0 + jl);
+#pragma unroll
+      for (int ig = 0; ig < T::IG; ++ig) {
+        if (row0 + i0 + ig * 16 + fr >= row_end) continue;
+#pragma unroll
+        for (int jg = 0; jg < T::JG; ++jg) rowp[ig][jg * 4] = codes4(acc[ig][jg]);  // 16 columns = 4 words
+      }
+    } else {
 #pragma unroll
     for (int ig = 0; ig < T::IG; ++ig) {
       const int i = row0 + i0 + ig * 16 + fr;
@@ -688,14 +727,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
       for (int jg = 0; jg < T::JG; ++jg) {
         const int j = col0 + j0 + jg * 16 + jl;
         if (j >= p.n) continue;
-        float q[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          q[r] = __fdiv_rn(acc[ig][jg][r], so);
-          if (!(fabsf(q[r]) <= kE4M3MaxOut) && q[r] == q[r]) q[r] = copysignf(kE4M3MaxOut, q[r]);  // saturate; NaN stays
-        }
-        int w4 = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
-        w4 = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w4, true);
+        const int w4 = codes4(acc[ig][jg]);
         if (vec) {
           *reinterpret_cast<int*>(orow + j) = w4;
         } else {
@@ -705,13 +737,45 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
         }
       }
     }
+    }  // columns reaching past n, or n not a multiple of 4
   } else {
   uint16_t* O = p.out + (int64_t)g * p.out_group_stride;
+  int row_id[T::IG];  // contiguous form: m_indices of each lane's rows, from the wave's registers
+#pragma unroll
+  for (int ig = 0; ig < T::IG; ++ig) row_id[ig] = CONTIG ? __shfl(wave_ids, ig * 16 + fr, 64) : 0;
+  auto pack4 = [&](const f32x4& a) {
+    uint2 v;
+    if (p.out_fp16) {
+      v.x = __builtin_bit_cast(uint32_t, f16x2{(_Float16)a[0], (_Float16)a[1]});
+      v.y = __builtin_bit_cast(uint32_t, f16x2{(_Float16)a[2], (_Float16)a[3]});
+    } else {
+      v.x = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a[0], (__bf16)a[1]});
+      v.y = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a[2], (__bf16)a[3]});
+    }
+    return v;
+  };
+  if (vec && col0 + j0 + T::WTN <= p.n) {
+    // All of the wave's columns are in range: each lane's row addresses are formed once, before
+    // the first store, and every store is an immediate offset from one of them. (A store whose
+    // address registers are overwritten must first complete, so recomputing one address register
+    // per store would make every store wait for the previous one.)
+    uint2* rowp[T::IG];
+#pragma unroll
+    for (int ig = 0; ig < T::IG; ++ig)
+      rowp[ig] = reinterpret_cast<uint2*>(O + (int64_t)(row0 + i0 + ig * 16 + fr) * p.n + col0 + j0 + jl);
+#pragma unroll
+    for (int ig = 0; ig < T::IG; ++ig) {
+      const int i = row0 + i0 + ig * 16 + fr;
+      if (!(i < row_end && (!CONTIG || row_id[ig] == bsel))) continue;
+#pragma unroll
+      for (int jg = 0; jg < T::JG; ++jg) rowp[ig][jg * 4] = pack4(acc[ig][jg]);  // 16 columns = 4 uint2
+    }
+  } else {
 #pragma unroll
   for (int ig = 0; ig < T::IG; ++ig) {
     const int i = row0 + i0 + ig * 16 + fr;
     bool ok = i < row_end;
-    if (CONTIG) ok = ok && p.rowinfo[i] == bsel;
+    if (CONTIG) ok = ok && row_id[ig] == bsel;
     if (!ok) continue;
     uint16_t* orow = O + (int64_t)i * p.n;
 #pragma unroll
@@ -740,6 +804,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
       }
     }
   }
+  }  // columns reaching past n, or n not a multiple of 4
   }  // 16-bit output
   }  // wave_live
 }
