@@ -151,7 +151,9 @@ moe_silu_mul_quant_kernel(const uint16_t* __restrict__ y, const int32_t* __restr
 }
 
 // One workgroup per token with one lane per 8 columns (up to 1024 lanes; wider rows loop). A lane
-// loads its 8 columns of up to 8 routed rows before the first FMA, then sums in slot order.
+// loads its 8 columns of up to 8 routed rows before the first FMA, then sums in slot order. The
+// loads are unconditional (a slot with no row reads row 0 and adds nothing), so all of them are
+// in flight together rather than each waiting behind its own branch.
 constexpr int kCombineBatch = 8;
 
 __global__ void __launch_bounds__(1024)
@@ -170,7 +172,7 @@ moe_combine_kernel(const uint16_t* __restrict__ y, const int32_t* __restrict__ r
       for (int j = 0; j < kCombineBatch; ++j) {
         const int r = s0 + j < top_k ? rows[s0 + j] : -1;
         live[j] = r >= 0 && r < m_alloc;
-        if (live[j]) raw[j] = *reinterpret_cast<const uint4*>(y + (int64_t)r * hidden + c);
+        raw[j] = *reinterpret_cast<const uint4*>(y + (int64_t)(live[j] ? r : 0) * hidden + c);
       }
 #pragma unroll
       for (int j = 0; j < kCombineBatch; ++j) {
@@ -230,6 +232,9 @@ hipError_t launch_moe_combine(const uint16_t* y, const int32_t* row_of_entry,
                               const float* topk_weights, int num_tokens, int top_k, int hidden,
                               int m_alloc, uint16_t* out, bool out_fp16, hipStream_t stream) {
   const int threads = std::min(1024, (hidden / 8 + 63) / 64 * 64);
+  // The kernel reads row 0 of y for slots with no row; with no rows at all no slot can hold one,
+  // and the output is zero, so it runs with no slots.
+  if (m_alloc == 0) top_k = 0;
   hipLaunchKernelGGL(moe_combine_kernel, dim3(num_tokens), dim3(threads), 0, stream, y, row_of_entry,
                      topk_weights, top_k, hidden, m_alloc, out, out_fp16);
   return hipGetLastError();
