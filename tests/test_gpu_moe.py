@@ -216,6 +216,31 @@ def test_moe_small_all_stages_and_end_to_end():
     assert err.max() <= 0.06 * rms and outside <= 0.05  # measured: 0.031 rms, 1.1% outside
 
 
+def test_combine_slots_without_rows_add_nothing():
+    """Slots with no row (-1, or an index at or beyond the rows) contribute nothing, even when the
+    row the kernel reads for them holds NaN; with no rows at all (m_alloc 0, through the C ABI) the
+    output is zero."""
+    say("combine: slots without rows")
+    from moe_expert_matmul_amd import _lib
+    h = 256
+    y = torch.randn((8, h), device=DEV).to(torch.bfloat16)
+    y[0] = float("nan")
+    roe = torch.tensor([[-1, 3], [9, 5], [3, 5]], dtype=torch.int32, device=DEV)
+    w = torch.tensor([[0.5, 0.25], [2.0, 1.0], [1.0, -1.0]], dtype=torch.float32, device=DEV)
+    out = torch.empty((3, h), dtype=torch.bfloat16, device=DEV)
+    fp8g.moe_combine(y, roe, w, out)
+    torch.cuda.synchronize()
+    y64 = bf16.from_bf16_bits(host(y))
+    ref = np.stack([0.25 * y64[3], 1.0 * y64[5], y64[3] - y64[5]])
+    assert_within_tolerance(bf16_values(out), ref, "combine")
+    out.fill_(1.0)
+    st = _lib.load().fp8_moe_combine(y.data_ptr(), roe.data_ptr(), w.data_ptr(), 3, 2, h, 0, out.data_ptr(), 0,
+                                      torch.cuda.current_stream().cuda_stream)
+    _lib.check(st, "fp8_moe_combine")
+    torch.cuda.synchronize()
+    assert not bf16_values(out).any(), "no rows: the output must be zero"
+
+
 def test_moe_unrouted_entries_and_empty_experts():
     say("moe with dropped entries and experts without tokens")
     d = workloads.moe(num_tokens=64, hidden=256, num_experts=6, top_k=2, inter=128, seed=2, device=DEV)
