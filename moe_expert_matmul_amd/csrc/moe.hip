@@ -18,14 +18,13 @@ namespace kernels {
 constexpr int kPermThreads = 1024;  // 16 waves
 constexpr int kPermWaves = kPermThreads / 64;
 constexpr int kMaxExperts = 1024;
-constexpr int kExpertBits = 10;      // ids below kMaxExperts
 constexpr int kPermBatch = 8;        // groups of 64 ids loaded together
 
-// Lanes of this wave whose (valid) id equals this lane's: one ballot per id bit.
-__device__ __forceinline__ uint64_t match_id(int id, bool valid) {
+// Lanes of this wave whose (valid) id equals this lane's: one ballot per id bit. Valid ids are
+// below num_experts, so bits from `bits` = ceil(log2(num_experts)) up are zero in all of them.
+__device__ __forceinline__ uint64_t match_id(int id, bool valid, int bits) {
   uint64_t m = __ballot(valid);
-#pragma unroll
-  for (int b = 0; b < kExpertBits; ++b) {
+  for (int b = 0; b < bits; ++b) {
     const uint64_t ones = __ballot(valid && ((id >> b) & 1));
     m &= ((id >> b) & 1) ? ones : ~ones;
   }
@@ -51,6 +50,7 @@ moe_permutation_kernel(const int32_t* __restrict__ ids, int entries, int top_k, 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint64_t lanes_below = (1ull << lane) - 1;
   const int chunk_begin = blockIdx.x * kPermThreads;
+  const int id_bits = num_experts > 1 ? 32 - __clz(num_experts - 1) : 0;  // wave-uniform
 
   for (int i = tid; i < kMaxExperts; i += kPermThreads) total_cnt[i] = before_cnt[i] = 0;
   for (int i = tid; i < kPermWaves * kMaxExperts; i += kPermThreads) (&group_cnt[0][0])[i] = 0;
@@ -68,7 +68,7 @@ moe_permutation_kernel(const int32_t* __restrict__ ids, int entries, int top_k, 
     for (int u = 0; u < kPermBatch; ++u) {
       const int id = idv[u];
       const bool valid = id >= 0 && id < num_experts;
-      const uint64_t same = match_id(id, valid);
+      const uint64_t same = match_id(id, valid, id_bits);
       if (valid && (same >> lane) == 1) {  // the last lane holding this expert adds for all of them
         atomicAdd(&total_cnt[id], __popcll(same));
         if (g0 + u * 64 < chunk_begin) atomicAdd(&before_cnt[id], __popcll(same));  // groups never straddle
@@ -78,7 +78,7 @@ moe_permutation_kernel(const int32_t* __restrict__ ids, int entries, int top_k, 
   const int idx = chunk_begin + wave * 64 + lane;  // this lane's entry of the chunk
   const int id = idx < entries ? ids[idx] : -1;
   const bool valid = id >= 0 && id < num_experts;
-  const uint64_t same = match_id(id, valid);
+  const uint64_t same = match_id(id, valid, id_bits);
   if (valid && (same >> lane) == 1) group_cnt[wave][id] = __popcll(same);
   __syncthreads();
 
