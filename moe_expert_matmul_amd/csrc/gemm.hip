@@ -307,8 +307,9 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   const int a_last = row_end - 1;
   // SWIGLU: b row of virtual column v of column tile tn (output columns [128 tn, 128 tn + 128))
   auto swiglu_b_row = [&](int v) {
-    const int q = v / (2 * OUTW), r = v % (2 * OUTW);
-    return (r < OUTW ? 0 : p.inter) + 128 * tn + q * OUTW + (r % OUTW);
+    constexpr int W = OUTW > 0 ? OUTW : 1;  // OUTW is 0 outside SWIGLU, where this is never called
+    const int q = v / (2 * W), r = v % (2 * W);
+    return (r < W ? 0 : p.inter) + 128 * tn + q * W + (r % W);
   };
   // The rows of a this lane's a loads read (entries 0 .. A_LOADS-1) and the row of a_scale its
   // scale load reads (entry A_LOADS, used by the a-scale waves): the tile rows themselves, or
