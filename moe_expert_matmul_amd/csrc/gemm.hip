@@ -267,6 +267,10 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
 #pragma unroll
     for (int q = 0; q < QUARTERS; ++q)
       tile_ids[q] = row0 + (q / 2) * 128 < p.m ? p.rowinfo[row0 + q * 64 + lane] : -1;
+    // ids outside [0, num_groups) are padding; mapped to -1 before the tile's expert (the largest
+    // id) is taken, so that a stray id cannot hide the rows of the half's real expert
+#pragma unroll
+    for (int q = 0; q < QUARTERS; ++q) tile_ids[q] = (unsigned)tile_ids[q] < (unsigned)p.num_groups ? tile_ids[q] : -1;
     if (p.a_rows != nullptr) {
 #pragma unroll
       for (int q = 0; q <= T::A_LOADS; ++q) gathered[q] = p.a_rows[a_tile_row(q, p.m - 1)];
@@ -274,8 +278,8 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     int ex[HALVES];
 #pragma unroll
     for (int h = 0; h < HALVES; ++h) {
-      const int e = __builtin_amdgcn_readfirstlane(wave_max(max(tile_ids[2 * h], tile_ids[2 * h + 1])));  // uniform: keeps b's resource scalar
-      ex[h] = (e >= 0 && e < p.num_groups) ? e : -1;  // -1: padding only
+      // uniform: keeps b's resource scalar; -1: padding only
+      ex[h] = __builtin_amdgcn_readfirstlane(wave_max(max(tile_ids[2 * h], tile_ids[2 * h + 1])));
     }
     if (HALVES == 2 && ex[0] >= 0 && ex[0] == ex[HALVES - 1]) {
       if (half == 1) return;

@@ -452,6 +452,32 @@ def test_contiguous_trailing_padding_tiles_and_poisoned_padding_rows():
     assert untouched(out)[host(pad)].all()
 
 
+@pytest.mark.parametrize("tile", ["128x256", "256x256"])
+def test_contiguous_out_of_range_ids_count_as_padding(tile):
+    """Indices outside [-1, num_groups) inside an expert's region are padding: that expert's rows
+    are still computed (a stray id larger than every expert must not take over the tile), and the
+    stray rows are never written."""
+    counts = [100, 40, 250, 7]
+    say("contiguous out-of-range ids", counts, tile)
+    d = workloads.contiguous(4, n=256, k=384, seed=41, device=DEV, counts=counts)
+    mi = host(d["m_indices"]).copy()
+    pad = np.nonzero(mi < 0)[0]
+    rng = np.random.default_rng(41)
+    stray = rng.choice(pad, min(len(pad), 40), replace=False)
+    mi[stray] = rng.choice(np.array([4, 9, 1 << 20, -2, -(1 << 30)], np.int32), stray.size)
+    d["m_indices"] = torch.from_numpy(mi).to(DEV)
+    try:
+        os.environ["FP8G_TILE"] = tile
+        out = _contig_call(d)
+    finally:
+        os.environ.pop("FP8G_TILE", None)
+    ref = _contig_ref(d)  # the oracle leaves rows with ids outside [0, 4) unspecified (NaN)
+    assert_within_tolerance(bf16_values(out), ref, "contiguous with out-of-range ids")
+    valid = (mi >= 0) & (mi < 4)
+    keep = untouched(out)
+    assert keep[~valid].all() and not keep[valid].any()
+
+
 def test_contiguous_mn_major_bitwise_equal():
     say("contiguous K vs MN")
     d = workloads.contiguous(3, n=256, k=512, seed=6, device=DEV, counts=[200, 64, 1])
