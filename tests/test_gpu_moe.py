@@ -1,11 +1,22 @@
 """GPU parity of the expert-FFN steps against the oracle, stage by stage (MI355X only).
 
 Integer work (the permutation) and the BF16 -> E4M3 quantiser of the tokens are compared bit for
-bit. The SiLU-mul quantiser is compared against the oracle fed the GPU's own fc1 output: both sides
-take the rounding decision in FP32, but SiLU's exp may differ by an ulp, so a code may differ by one
-step where the oracle's scaled value lies within a few FP32 ulps of the midpoint between two codes;
-every other code and every scale must match. The GEMMs and the combine are held to the GEMM
-tolerance on the oracle fed the GPU's own inputs.
+bit. The GEMMs and the combine are held to the GEMM tolerance on the oracle fed the GPU's own inputs.
+
+The SiLU-mul requantisation is compared against the oracle fed the GPU's own BF16 fc1 output, with
+an error budget derived from the kernel's arithmetic (u = 2^-24, the FP32 unit roundoff):
+  - the kernel's silu(g) = g / (1 + expf(-g)) lies within 2.25 u (relative) of the exact value for
+    every BF16 g >= -88.5; that was measured exhaustively over all BF16 inputs (largest 2.21 u). Below,
+    expf(-g) overflows and the kernel returns -0 where |silu(g)| < 2e-37, which cannot set a block's
+    maximum nor lie near a code boundary for any block with a value above 1e-30;
+  - h = silu(g) * up adds one rounding, and the oracle rounds the exact h to FP32 once, so the two h
+    differ by at most H_REL = 4.25 u of h;
+  - a block's amax inherits that, and scale = amax / 448 adds one rounding per side: the scales
+    differ by less than 6.5 u of the scale, i.e. by at most SCALE_ULPS whole FP32 ulps;
+  - the quotients h / scale differ by at most QUOT_REL = 12.5 u relative, so a code may differ by one
+    step only where the oracle's quotient lies within QUOT_REL of the midpoint between two codes.
+    Midpoints are at least 1/16 of the value apart, so at most 2 * 16 * QUOT_REL (2.4e-5) of the codes
+    can lie that close: more than FLIP_FRACTION = 1e-4 flipped codes means a wrong quantiser.
 """
 
 import os
@@ -17,7 +28,7 @@ import torch
 import moe_expert_matmul_amd as fp8g
 import workloads
 from oracle import bf16, e4m3, gemm as ogemm, moe as omoe
-from parity import assert_within_tolerance, bf16_values, host, say
+from parity import assert_within_tolerance, bf16_values, combine_bound, host, record, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -63,21 +74,38 @@ def _sliced_ref(a, sa, b, sb, m_indices, rows, col_blocks):
     return ogemm.group_gemm_contiguous(a, b[:, cols], sa, sb[:, col_blocks], m_indices, rows=rows), cols
 
 
-def _check_requant(y1_rows, a2_rows, sa2_rows):
-    """Oracle quantiser on the GPU's fc1 rows; allows one-step flips at FP32 rounding midpoints."""
-    h32 = omoe.silu_mul(bf16.from_bf16_bits(y1_rows)).astype(np.float32)
-    oc, osc = omoe.quantize_1x128(h32)
-    assert np.allclose(sa2_rows, osc, rtol=4e-7, atol=0), "requant scales differ by more than an ulp"
-    diff = a2_rows != oc
-    if diff.any():
-        x = (h32 / np.repeat(osc, 128, axis=1))[diff].astype(np.float64)
-        g = e4m3.decode(a2_rows[diff])
-        o = e4m3.decode(oc[diff])
-        mid = (g + o) / 2
-        assert np.all(np.abs(np.abs(g) - np.abs(o)) <= np.maximum(np.abs(g), np.abs(o)) / 8 + 2.0 ** -9)
-        assert np.all(np.abs(x - mid) <= 1e-5 * np.abs(x) + 1e-12), "a code differs away from a rounding midpoint"
-        assert diff.mean() <= 1e-3
-    return int(diff.sum())
+U = 2.0 ** -24  # FP32 unit roundoff
+H_REL = 4.25 * U  # kernel h against float32(exact h)
+SCALE_ULPS = 6   # |scale difference| < 6.5 u of the scale
+QUOT_REL = H_REL + (H_REL + 2 * U) + 2 * U  # both scales, one division per side
+FLIP_FRACTION = 1e-4
+
+
+def _check_requant(y1_rows, a2_rows, sa2_rows, chunk=2048):
+    """Oracle quantiser on the GPU's BF16 fc1 rows against the GPU's codes and scales, within the error
+    budget above; rows in chunks to bound host memory. Returns (codes compared, codes flipped, largest
+    scale difference in ulps)."""
+    n_codes, flips, worst_ulps = 0, 0, 0
+    for r0 in range(0, y1_rows.shape[0], chunk):
+        y1, a2, sa2 = y1_rows[r0:r0 + chunk], a2_rows[r0:r0 + chunk], sa2_rows[r0:r0 + chunk]
+        h32 = omoe.silu_mul(bf16.from_bf16_bits(y1)).astype(np.float32)
+        oc, osc = omoe.quantize_1x128(h32)
+        ulps = np.abs(sa2.astype(np.float32).view(np.int32).astype(np.int64) - osc.view(np.int32).astype(np.int64))
+        worst_ulps = max(worst_ulps, int(ulps.max()))
+        assert ulps.max() <= SCALE_ULPS, f"requant scales differ by {ulps.max()} ulps (budget {SCALE_ULPS})"
+        diff = a2 != oc
+        n_codes += a2.size
+        if diff.any():
+            g, o = a2[diff].astype(np.int32), oc[diff].astype(np.int32)
+            assert np.all((g & 0x80) == (o & 0x80)) and np.all(np.abs((g & 0x7F) - (o & 0x7F)) == 1), \
+                "a code differs from the oracle's by more than one step"
+            x = (h32 / np.repeat(osc, 128, axis=1))[diff].astype(np.float64)  # the oracle's quotients
+            mid = (e4m3.decode(a2[diff]) + e4m3.decode(oc[diff])) / 2
+            far = np.abs(x - mid) > QUOT_REL * np.abs(x)
+            assert not far.any(), f"{int(far.sum())} codes differ away from a rounding midpoint"
+            flips += int(diff.sum())
+    assert flips <= FLIP_FRACTION * n_codes, f"{flips} of {n_codes} codes flipped (budget {FLIP_FRACTION:g})"
+    return n_codes, flips, worst_ulps
 
 
 def _stagewise(d, out, ws, p, rows, token_sample, col_blocks_fc1, col_blocks_fc2):
@@ -89,8 +117,9 @@ def _stagewise(d, out, ws, p, rows, token_sample, col_blocks_fc1, col_blocks_fc2
     # fc1 on the GPU's own quantised tokens, in the permuted order
     ref, cols = _sliced_ref(a1, sa1, w1, s1, mi, rows, col_blocks_fc1)
     assert_within_tolerance(bf16.from_bf16_bits(y1_bits[rows][:, cols]), ref, "fc1")
-    # SiLU-mul + requant on the GPU's own fc1 output
-    flips = _check_requant(y1_bits[rows], host(ws.a2)[rows], host(ws.sa2)[rows])
+    # SiLU-mul + requant on the GPU's own fc1 output, every valid row
+    valid = np.nonzero(mi >= 0)[0]
+    requant = _check_requant(y1_bits[valid], host(ws.a2)[valid], host(ws.sa2)[valid])
     # fc2 on the GPU's own requantised activations
     ref, cols = _sliced_ref(host(ws.a2), host(ws.sa2), w2, s2, mi, rows, col_blocks_fc2)
     assert_within_tolerance(bf16.from_bf16_bits(host(ws.y2)[rows][:, cols]), ref, "fc2")
@@ -100,7 +129,7 @@ def _stagewise(d, out, ws, p, rows, token_sample, col_blocks_fc1, col_blocks_fc2
     compact = np.where(roe >= 0, np.arange(roe.size).reshape(roe.shape), -1)
     ref = omoe.combine(y2_rows, compact, host(d["topk_weights"])[token_sample])
     assert_within_tolerance(bf16_values(out)[token_sample], ref, "combine")
-    return flips
+    return dict(zip(("codes", "code_flips", "scale_ulps_max"), requant))
 
 
 def test_moe_expert_parallel_shard_sampled():
@@ -129,15 +158,16 @@ def test_moe_expert_parallel_shard_sampled():
     remote_only = np.nonzero((ids >= shard).all(axis=1))[0]
     assert remote_only.size > 0
     tokens = np.unique(np.concatenate([[0, 4095], remote_only[:3], rng.choice(4096, 11, replace=False)]))
-    flips = _stagewise(d, out, ws, p, rows, tokens, [0, 16, 31], [0, 27, 55])
+    stats = _stagewise(d, out, ws, p, rows, tokens, [0, 16, 31], [0, 27, 55])
     assert not bf16_values(out)[remote_only].any(), "tokens with no local route must come out zero"
-    say("requant code flips on sampled rows", flips)
+    record("moe expert-parallel shard 8 of 64 experts, requant", **stats)
 
 
 @pytest.mark.parametrize("num_tokens,top_k,num_experts", [(1, 1, 1), (5, 3, 7), (777, 1, 1024), (4096, 8, 64),
-                                                            (20000, 6, 129)])
+                                                            (20000, 6, 129), (65536, 8, 256), (300, 4, 1)])
 def test_permutation_matches_oracle(num_tokens, top_k, num_experts):
-    """The permutation alone: odd sizes, one expert, 1024 experts, ~5% unrouted (-1 or out-of-range) ids."""
+    """The permutation alone: odd sizes, one expert, 1024 experts, 512 chunks of entries, ~5% unrouted
+    (-1 or out-of-range) ids."""
     say("permutation", num_tokens, top_k, num_experts)
     rng = np.random.default_rng(num_tokens + 7 * num_experts)
     ids = np.stack([rng.permutation(num_experts)[:top_k] if top_k <= num_experts else
@@ -199,21 +229,32 @@ def test_moe_small_all_stages_and_end_to_end():
     p = _check_permutation(d, ws)
     _check_gather_quant(d, ws, p)
     rows = np.nonzero(p["m_indices"] >= 0)[0]
-    flips = _stagewise(d, out, ws, p, rows, np.arange(256), [0, 1, 2, 3], [0, 1, 2, 3])
-    say("requant code flips", flips)
-    # End to end against the all-oracle chain. The requantisation between fc1 and fc2 is
-    # discontinuous: fc1 outputs that differ in their last BF16 bit (FP32 accumulation order) can
-    # land on different E4M3 codes, each a step of up to 1/8 of the value, so the chain is not held
-    # to the GEMM tolerance. It is reported, and bounded well above the flip noise (a wrong stage
-    # -- gate/up swapped, a missing weight, a wrong row -- gives errors of the order of rms).
+    stats = _stagewise(d, out, ws, p, rows, np.arange(256), [0, 1, 2, 3], [0, 1, 2, 3])
+    # End to end against the all-oracle chain. The two chains differ only where their activation
+    # codes differ: fc1 values that differ in their last BF16 bit (FP32 accumulation order) can
+    # round to different E4M3 codes, each a step of up to 1/8 of the value. That difference is
+    # reported, not graded. What is checked is the decomposition: the oracle's fc2 and combine run on
+    # the GPU's own activation codes give the GPU's output within the fc2 tolerance carried through
+    # the weighted sum (plus the combine's own), so the rest of the difference is the part the
+    # differing codes account for.
     r = omoe.moe_ffn(bf16.from_bf16_bits(host(d["x"])), host(d["topk_ids"]), host(d["topk_weights"]),
                      host(d["w1"]), host(d["s1"]), host(d["w2"]), host(d["s2"]), m_alloc=ws.m_alloc)
+    mi = p["m_indices"]
+    y2_exact = ogemm.group_gemm_contiguous(host(ws.a2), host(d["w2"]), host(ws.sa2), host(d["s2"]), mi)
+    on_gpu_codes = omoe.combine(np.nan_to_num(bf16.round_to_bf16(y2_exact)), p["row_of_entry"],
+                                host(d["topk_weights"]))
     got, ref = bf16_values(out), r["out"]
+    bound = combine_bound(np.nan_to_num(y2_exact), p["row_of_entry"], host(d["topk_weights"]), on_gpu_codes)
+    bad = np.abs(got - on_gpu_codes) > bound
+    assert not bad.any(), f"end to end on the GPU's codes: {int(bad.sum())} outputs beyond the carried tolerance"
     rms = float(np.sqrt(np.mean(ref ** 2)))
     err = np.abs(got - ref)
-    outside = float(np.mean(err > 8e-3 * np.abs(ref) + 1e-3 * rms))
-    say(f"moe end to end: max err {err.max() / rms:.4f} rms, {outside:.4%} outside the GEMM tolerance")
-    assert err.max() <= 0.06 * rms and outside <= 0.05  # measured: 0.031 rms, 1.1% outside
+    valid = mi >= 0
+    record("moe small T=256 H=512 E=8 k=2 I=256, end to end", **stats,
+           codes_differing_from_oracle_chain=int((host(ws.a2)[valid] != r["a2"][valid]).sum()),
+           max_err_vs_oracle_chain_rms=round(float(err.max()) / rms, 5),
+           max_part_of_differing_codes_rms=round(float(np.abs(on_gpu_codes - ref).max()) / rms, 5),
+           fraction_outside_gemm_tolerance=round(float(np.mean(err > 8e-3 * np.abs(ref) + 1e-3 * rms)), 5))
 
 
 def test_combine_slots_without_rows_add_nothing():
@@ -273,5 +314,5 @@ def test_moe_full_size_stagewise_sampled():
     rows += rng.choice(np.nonzero(mi >= 0)[0], 6, replace=False).tolist()
     rows = np.unique(np.array(rows))
     tokens = np.unique(np.concatenate([[0, 4095], rng.choice(4096, 14, replace=False)]))
-    flips = _stagewise(d, out, ws, p, rows, tokens, [0, 16, 31], [0, 27, 55])
-    say("requant code flips on sampled rows", flips)
+    stats = _stagewise(d, out, ws, p, rows, tokens, [0, 16, 31], [0, 27, 55])
+    record("moe full size T=4096 H=7168 E=64 k=8 I=2048, requant", **stats)

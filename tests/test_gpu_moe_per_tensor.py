@@ -13,8 +13,8 @@ import torch
 
 import moe_expert_matmul_amd as fp8g
 import workloads
-from oracle import e4m3, moe as omoe
-from parity import assert_within_tolerance, bf16_values, fp16_values, host, say
+from oracle import bf16, e4m3, moe as omoe
+from parity import assert_within_tolerance, bf16_values, combine_bound, fp16_values, host, record, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -81,9 +81,11 @@ def test_per_tensor_ffn_stages(case):
     assert np.mean(got != omoe.quantize_per_tensor(q)) < 1e-2
     # (ii) fc2 on the GPU's own codes
     y2_ref = omoe.fc2_per_tensor(host(ws.a2)[rows], sub["m_indices"], host(d["w2"]), host(d["fc2_dequant"]))
-    assert_within_tolerance(bf16_values(ws.y2)[rows], y2_ref, f"per-tensor fc2 {case}")
+    assert_within_tolerance(bf16.from_bf16_bits(host(ws.y2)[rows]), y2_ref, f"per-tensor fc2 {case}")
     # (iii) combine (weight 1) on the GPU's own fc2 output
-    ref = omoe.combine(np.nan_to_num(np.where(valid[:, None], bf16_values(ws.y2), 0.0)), perm["row_of_entry"], None)
+    # padding rows of y2 are unspecified: their bits are masked before the BF16 decode
+    y2 = bf16.from_bf16_bits(np.where(valid[:, None], host(ws.y2), np.uint16(0)))
+    ref = omoe.combine(y2, perm["row_of_entry"], None)
     assert_within_tolerance(bf16_values(out), ref, f"per-tensor combine {case}")
 
 
@@ -103,20 +105,37 @@ def test_per_tensor_fc2_quant_per_expert_and_fp16_out_with_weights():
                                    host(d["fc1_dequant"]), host(qs))
     got = host(ws.a2)[valid]
     assert np.mean(got != omoe.quantize_per_tensor(q[valid])) < 1e-2
-    ref = omoe.combine(np.where(valid[:, None], bf16_values(ws.y2), 0.0), perm["row_of_entry"], host(d["topk_weights"]))
+    y2 = bf16.from_bf16_bits(np.where(valid[:, None], host(ws.y2), np.uint16(0)))  # padding rows: unspecified
+    ref = omoe.combine(y2, perm["row_of_entry"], host(d["topk_weights"]))
     assert_within_tolerance(fp16_values(out), ref, "per-tensor combine fp16")
 
 
 def test_per_tensor_end_to_end_against_the_oracle_chain():
-    """Reported bound: the all-oracle chain differs from the GPU chain only through activation codes
-    that flip near rounding midpoints."""
+    """The all-oracle chain differs from the GPU chain only through activation codes that flip near
+    rounding midpoints (the GPU decides them from FP32 sums). That difference is reported, not graded;
+    what is checked is the decomposition: the oracle's fc2 and combine run on the GPU's own codes give
+    the GPU's output within the GEMM tolerance."""
     say("per-tensor end to end")
     d = workloads.moe_per_tensor(256, 512, 8, 2, 256, seed=6, device=DEV)
+    ws = fp8g.MoePerTensorWorkspace.allocate(256, 2, 8, 512, 256, DEV)
     out = fp8g.moe_ffn_fp8_per_tensor(d["x"], d["topk_ids"], d["w1"], d["w2"], d["fc1_dequant"], d["fc2_quant"],
-                                      d["fc2_dequant"])
+                                      d["fc2_dequant"], workspace=ws)
     torch.cuda.synchronize()
     r = omoe.moe_ffn_per_tensor(host(d["x"]), host(d["topk_ids"]), host(d["w1"]), host(d["w2"]),
-                                host(d["fc1_dequant"]), host(d["fc2_quant"]), host(d["fc2_dequant"]))
+                                host(d["fc1_dequant"]), host(d["fc2_quant"]), host(d["fc2_dequant"]),
+                                m_alloc=ws.m_alloc)
+    mi = r["perm"]["m_indices"]
+    assert np.array_equal(host(ws.m_indices), mi)
+    y2_exact = omoe.fc2_per_tensor(host(ws.a2), mi, host(d["w2"]), host(d["fc2_dequant"]))
+    on_gpu_codes = omoe.combine(np.nan_to_num(bf16.round_to_bf16(y2_exact)), r["perm"]["row_of_entry"], None)
     got, ref = bf16_values(out), r["out"]
-    rms = np.sqrt(np.mean(ref ** 2))
-    assert np.max(np.abs(got - ref)) <= 0.06 * rms
+    bound = combine_bound(np.nan_to_num(y2_exact), r["perm"]["row_of_entry"], None, on_gpu_codes)
+    bad = np.abs(got - on_gpu_codes) > bound
+    assert not bad.any(), f"per-tensor end to end on the GPU's codes: {int(bad.sum())} outputs beyond the carried tolerance"
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    valid = mi >= 0
+    record("per-tensor moe T=256 H=512 E=8 k=2 I=256, end to end",
+           codes_differing_from_oracle_chain=int((host(ws.a2)[valid] != r["a2"][valid]).sum()),
+           codes=int(valid.sum()) * 256,
+           max_err_vs_oracle_chain_rms=round(float(np.abs(got - ref).max()) / rms, 5),
+           max_part_of_differing_codes_rms=round(float(np.abs(on_gpu_codes - ref).max()) / rms, 5))
