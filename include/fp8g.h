@@ -23,7 +23,9 @@
  *
  * Scale granularity: only (gran_m, gran_n, gran_k) = (1, 128, 128) -- one FP32 scale per row and
  * 128-wide K block of `a`, one per 128x128 block of `b` -- is implemented; any other value returns
- * FP8G_NOT_SUPPORTED. k must be a multiple of 128 and n a multiple of 128.
+ * FP8G_NOT_SUPPORTED. k must be a multiple of 128 in every form; n must be a multiple of 128 in the
+ * grouped and masked forms (the plain form takes any n: its last b-scale block may cover fewer than
+ * 128 rows of b).
  *
  * Arithmetic (MATE FlashInfer-API page, section "GEMM"): for every output element
  *     out[i][j] = cvt( sum_kb  sa(i,kb) * sb(j/128,kb) * sum_{k in block kb} a[i][k] * b[j][k] )
@@ -70,6 +72,19 @@ FP8G_API const char* fp8g_last_error(void);
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 FP8G_API int32_t fp8g_version(void);
+
+/*
+ * Measurement aid (not part of the method): the shader clock the device runs at. Enqueues on
+ * `stream` one single-wave kernel that spins for about spin_us (0 .. 100000) microseconds of the
+ * device's constant-rate wall clock and writes to out (device memory, two uint64, 8-byte aligned)
+ * the shader-clock cycles and the wall-clock ticks that passed. The average shader clock in kHz is
+ * out[0] / out[1] * fp8g_wall_clock_khz(). Enqueued right after a timed region it reads the clock
+ * the part settled at under that load.
+ */
+FP8G_API fp8g_status_t fp8g_clock_probe(unsigned long long* out, int64_t spin_us, void* stream);
+
+/* Rate of the current device's wall clock (hipDeviceAttributeWallClockRate) in kHz; -1 on error. */
+FP8G_API int64_t fp8g_wall_clock_khz(void);
 
 /*
  * Plain form: out = a @ b.T with groupwise scales.
@@ -228,7 +243,8 @@ FP8G_API fp8g_status_t fp8_fused_add_rmsnorm_quant(void* out, float* block_scale
  * ------------------------------------------------------------------------------------------- */
 
 /*
- * Group the (token, slot) entries of topk_ids by expert into the contiguous grouped layout.
+ * Group the (token, slot) entries of topk_ids by expert into the contiguous grouped layout (the
+ * m_indices of the MATE FlashInfer-API page's group_deepgemm_fp8_nt_groupwise, section "GEMM").
  *   topk_ids      (num_tokens, top_k) int32 expert ids in [0, num_experts); other values are
  *                 dropped (routed nowhere)
  *   m_indices     (m_alloc,) int32 out: expert e owns rows [off_e, off_e + ceil(c_e/128)*128) in
@@ -237,13 +253,20 @@ FP8G_API fp8g_status_t fp8_fused_add_rmsnorm_quant(void* out, float* block_scale
  *                 last region are -1
  *   src_token     (m_alloc,) int32 out: token of each row, -1 for padding
  *   row_of_entry  (num_tokens, top_k) int32 out: row of each entry, -1 if the entry was dropped
+ *   workspace     device scratch of at least fp8_moe_permutation_workspace_size(num_tokens, top_k,
+ *                 num_experts) bytes, 4-byte aligned (may be NULL when that size is 0); it holds
+ *                 per-chunk expert counts between the call's kernels, needs no initialisation, and
+ *                 must not be used by another call until this one has finished on `stream`
  * m_alloc must be at least num_tokens*top_k + num_experts*127 (rounded up to 128) so that every
- * routing fits; it must be a multiple of 128. num_experts <= 1024. Deterministic.
+ * routing fits; it must be a multiple of 128. num_experts <= 1024. Deterministic; the work is linear
+ * in num_tokens*top_k (three kernels: per-chunk counts, one scan, per-chunk placement).
  */
+FP8G_API int64_t fp8_moe_permutation_workspace_size(int64_t num_tokens, int64_t top_k, int64_t num_experts);
 FP8G_API fp8g_status_t fp8_moe_build_permutation(const int32_t* topk_ids, int64_t num_tokens,
                                         int64_t top_k, int64_t num_experts, int64_t m_alloc,
                                         int32_t* m_indices, int32_t* src_token,
-                                        int32_t* row_of_entry, void* stream);
+                                        int32_t* row_of_entry, void* workspace, int64_t workspace_bytes,
+                                        void* stream);
 
 /*
  * Quantise BF16 token rows per 1x128 block into the permuted layout:

@@ -31,5 +31,6 @@ from .moe import (  # noqa: F401
     moe_ffn_fp8_per_tensor,
     moe_gather_quant,
     moe_silu_mul_quant,
+    permutation_workspace_bytes,
 )
 from .quant import fp8_quantize_1x128, fused_add_rmsnorm_fp8_block_quant  # noqa: F401

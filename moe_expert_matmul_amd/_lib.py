@@ -24,6 +24,8 @@ _I32 = ctypes.c_int32
 SIGNATURES = {
     "fp8g_last_error": ([], ctypes.c_char_p),
     "fp8g_version": ([], _I32),
+    "fp8g_clock_probe": ([_P, _I64, _P], _I32),
+    "fp8g_wall_clock_khz": ([], _I64),
     "fp8_gemm_nt_groupwise": ([_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P], _I32),
     "fp8_gemm_nt_groupwise_fp8_out": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P], _I32),
     "fp8_group_gemm_contiguous": ([_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P],
@@ -36,7 +38,8 @@ SIGNATURES = {
     "fp8_bmm": ([_P, _P, _P, _I32, _P, _I32, _P, _I32, _I64, _I64, _I64, _I64, _P, _I64, _P], _I32),
     "fp8_quantize_1x128": ([_P, _I64, _I64, _P, _P, _I32, _P], _I32),
     "fp8_fused_add_rmsnorm_quant": ([_P, _P, _P, _P, _P, _P, ctypes.c_float, _I64, _I64, _I32, _P], _I32),
-    "fp8_moe_build_permutation": ([_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P], _I32),
+    "fp8_moe_permutation_workspace_size": ([_I64, _I64, _I64], _I64),
+    "fp8_moe_build_permutation": ([_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _I64, _P], _I32),
     "fp8_moe_gather_quant": ([_P, _P, _I64, _I64, _I64, _P, _P, _P], _I32),
     "fp8_moe_silu_mul_quant": ([_P, _P, _I64, _I64, _P, _P, _P], _I32),
     "fp8_moe_fc1_silu_quant": ([_P, _P, _I64, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32,

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libfp8g.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["api.hip", "gemm.hip", "moe.hip", "quant.hip", "bmm.hip"]
+SOURCES = ["api.hip", "gemm.hip", "moe.hip", "quant.hip", "bmm.hip", "clock.hip"]
 
 ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -157,9 +157,59 @@ int fp8g::tile_override() {
   return -1;
 }
 
+namespace {
+
+const char* mode_name(fp8g::GemmMode mode) {
+  switch (mode) {
+    case fp8g::MODE_PLAIN: return "plain";
+    case fp8g::MODE_CONTIG: return "contiguous";
+    case fp8g::MODE_MASKED: return "masked";
+    case fp8g::MODE_CONTIG_SWIGLU: return "contiguous+silu-quant";
+    case fp8g::MODE_BMM: return "bmm";
+    case fp8g::MODE_CONTIG_PT: return "contiguous per-tensor";
+    case fp8g::MODE_CONTIG_PT_SWIGLU: return "contiguous per-tensor+silu-quant";
+  }
+  return "?";
+}
+
+// Launch a GEMM; with FP8G_LOG set (to anything but "0") the call, its sizes and the tile
+// configuration chosen are written to stderr first. Read at every call, like FP8G_TILE.
+void launch_logged(const char* what, fp8g::GemmMode mode, fp8g::TileConfig cfg, const fp8g::GemmParams& p,
+                   int64_t grid, void* stream) {
+  const char* env = std::getenv("FP8G_LOG");
+  if (env && *env && std::strcmp(env, "0") != 0)
+    std::fprintf(stderr, "fp8g: %s [%s] m=%d n=%d k=%d groups=%d tile=%dx%d grid=%lld tiles=%dx%d stream=%p\n", what,
+                 mode_name(mode), p.m, p.n, p.k, p.num_groups, fp8g::tile_rows(cfg), fp8g::tile_cols(cfg),
+                 (long long)grid, p.tiles_m, p.tiles_n, stream);
+  check_hip(fp8g::launch_gemm(mode, cfg, p, (int)grid, (hipStream_t)stream), what);
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* fp8g_last_error(void) { return g_last_error.c_str(); }
+
+fp8g_status_t fp8g_clock_probe(unsigned long long* out, int64_t spin_us, void* stream) {
+  return guarded([&] {
+    require(out != nullptr && aligned(out, 8), "out must be non-null and 8-byte aligned");
+    require(spin_us >= 0 && spin_us <= 100000, "spin_us must be in [0, 100000]");
+    check_device();
+    int dev = 0, khz = 0;
+    check_hip(hipGetDevice(&dev), "hipGetDevice");
+    check_hip(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev), "wall clock rate");
+    check_hip(fp8g::launch_clock_probe(out, (unsigned long long)spin_us * (unsigned long long)khz / 1000,
+                                       (hipStream_t)stream),
+              "fp8g_clock_probe launch");
+  });
+}
+
+int64_t fp8g_wall_clock_khz(void) {
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return -1;
+  return khz;
+}
 
 int32_t fp8g_version(void) { return 100; }  // 0.1.0
 
@@ -200,7 +250,7 @@ void plain_gemm(const void* a, const void* b, const float* a_scale, const float*
   p.tiles_n = (int32_t)ceil_div(n, fp8g::tile_cols(cfg));
   p.group_m = 4;
   const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
-  check_hip(fp8g::launch_gemm(fp8g::MODE_PLAIN, cfg, p, (int)grid, (hipStream_t)stream), what);
+  launch_logged(what, fp8g::MODE_PLAIN, cfg, p, grid, stream);
 }
 
 }  // namespace
@@ -320,7 +370,7 @@ void group_gemm_contiguous(const void* a, const float* a_scale, int64_t a_src_ro
   require(grid <= kInt32Max, "too many tiles");
   const fp8g::GemmMode mode = pt ? (swiglu ? fp8g::MODE_CONTIG_PT_SWIGLU : fp8g::MODE_CONTIG_PT)
                                  : (swiglu ? fp8g::MODE_CONTIG_SWIGLU : fp8g::MODE_CONTIG);
-  check_hip(fp8g::launch_gemm(mode, cfg, p, (int)grid, (hipStream_t)stream), what);
+  launch_logged(what, mode, cfg, p, grid, stream);
 }
 
 }  // namespace
@@ -452,32 +502,60 @@ fp8g_status_t fp8_batch_gemm_masked(const void* a, const void* b, const float* a
     p.group_m = p.tiles_m;
     const int64_t grid = (int64_t)num_groups * p.tiles_m * p.tiles_n;
     require(grid <= kInt32Max, "too many tiles");
-    check_hip(fp8g::launch_gemm(fp8g::MODE_MASKED, cfg, p, (int)grid, (hipStream_t)stream),
-              "fp8_batch_gemm_masked launch");
+    launch_logged("fp8_batch_gemm_masked launch", fp8g::MODE_MASKED, cfg, p, grid, stream);
   });
 }
+
+int64_t fp8_moe_permutation_workspace_size(int64_t num_tokens, int64_t top_k, int64_t num_experts) {
+  if (num_tokens < 0 || top_k < 0 || num_experts < 1 || num_experts > 1024 || num_tokens * top_k > kInt32Max)
+    return -1;
+  return 4 * fp8g::moe_permutation_scratch_ints(num_tokens * top_k, num_experts);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the permutation entry points; returns false when there is nothing to do.
+bool check_permutation(const int32_t* topk_ids, int64_t num_tokens, int64_t top_k, int64_t num_experts,
+                       int64_t m_alloc, const int32_t* m_indices, const int32_t* src_token,
+                       const int32_t* row_of_entry) {
+  require(num_tokens >= 0 && top_k >= 0 && num_experts >= 1 && m_alloc >= 0, "sizes must be non-negative, num_experts >= 1");
+  require(num_experts <= 1024, "num_experts must be at most 1024");
+  require(num_tokens * top_k <= kInt32Max && m_alloc <= kInt32Max, "sizes must fit in int32");
+  require(m_alloc % 128 == 0, "m_alloc must be a multiple of 128");
+  const int64_t need = ceil_div(num_tokens * top_k + num_experts * 127, 128) * 128;
+  require(m_alloc >= need, "m_alloc (%lld) must be at least %lld for this many entries and experts",
+          (long long)m_alloc, (long long)need);
+  if (m_alloc == 0) return false;
+  require(m_indices && src_token && (num_tokens * top_k == 0 || (topk_ids && row_of_entry)),
+          "pointers must be non-null");
+  require(aligned(topk_ids, 4) && aligned(m_indices, 4) && aligned(src_token, 4) && aligned(row_of_entry, 4),
+          "pointers must be 4-byte aligned");
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
 
 fp8g_status_t fp8_moe_build_permutation(const int32_t* topk_ids, int64_t num_tokens,
                                         int64_t top_k, int64_t num_experts, int64_t m_alloc,
                                         int32_t* m_indices, int32_t* src_token,
-                                        int32_t* row_of_entry, void* stream) {
+                                        int32_t* row_of_entry, void* workspace, int64_t workspace_bytes,
+                                        void* stream) {
   return guarded([&] {
-    require(num_tokens >= 0 && top_k >= 0 && num_experts >= 1 && m_alloc >= 0, "sizes must be non-negative, num_experts >= 1");
-    require(num_experts <= 1024, "num_experts must be at most 1024");
-    require(num_tokens * top_k <= kInt32Max && m_alloc <= kInt32Max, "sizes must fit in int32");
-    require(m_alloc % 128 == 0, "m_alloc must be a multiple of 128");
-    const int64_t need = ceil_div(num_tokens * top_k + num_experts * 127, 128) * 128;
-    require(m_alloc >= need, "m_alloc (%lld) must be at least %lld for this many entries and experts",
-            (long long)m_alloc, (long long)need);
-    if (m_alloc == 0) return;
-    require(m_indices && src_token && (num_tokens * top_k == 0 || (topk_ids && row_of_entry)),
-            "pointers must be non-null");
-    require(aligned(topk_ids, 4) && aligned(m_indices, 4) && aligned(src_token, 4) && aligned(row_of_entry, 4),
-            "pointers must be 4-byte aligned");
+    if (!check_permutation(topk_ids, num_tokens, top_k, num_experts, m_alloc, m_indices, src_token, row_of_entry))
+      return;
+    const int64_t need = 4 * fp8g::moe_permutation_scratch_ints(num_tokens * top_k, num_experts);
+    require(workspace_bytes >= need, "workspace (%lld bytes) must hold %lld bytes", (long long)workspace_bytes,
+            (long long)need);
+    require(need == 0 || (workspace != nullptr && aligned(workspace, 4)),
+            "workspace must be non-null and 4-byte aligned");
     check_device();
     check_hip(fp8g::launch_moe_build_permutation(topk_ids, (int)num_tokens, (int)top_k, (int)num_experts,
                                                  (int)m_alloc, m_indices, src_token, row_of_entry,
-                                                 (hipStream_t)stream),
+                                                 static_cast<int32_t*>(workspace), (hipStream_t)stream),
               "fp8_moe_build_permutation launch");
   });
 }
@@ -558,7 +636,7 @@ fp8g_status_t fp8_bmm(const void* a, const void* b, const float* a_scale, int32_
     p.group_m = 4;
     const int64_t grid = batch * p.tiles_m * p.tiles_n;
     require(grid <= kInt32Max, "too many tiles");
-    check_hip(fp8g::launch_gemm(fp8g::MODE_BMM, cfg, p, (int)grid, (hipStream_t)stream), "fp8_bmm launch");
+    launch_logged("fp8_bmm launch", fp8g::MODE_BMM, cfg, p, grid, stream);
   });
 }
 

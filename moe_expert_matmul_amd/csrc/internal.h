@@ -64,7 +64,10 @@ enum TileConfig : int {
 
 // Tile configuration forced through the FP8G_TILE environment variable ("256x256", "128x256",
 // "256x128", "128x128"), read at every call; -1 when unset. For tuning and for the tests that check that
-// results never depend on the tile. The contiguous form always uses 128-row tiles.
+// results never depend on the tile. The contiguous form uses 128x256 tiles by default and 256x256
+// tiles for short K with large expert regions (k <= 2048 and at least 512 rows per expert on
+// average); with 256-row tiles the grid holds one entry per 128-row half, and a tile whose halves
+// belong to different experts runs as two workgroups, each covering its own half.
 int tile_override();
 
 int tile_rows(TileConfig cfg);
@@ -82,9 +85,11 @@ hipError_t launch_fused_add_rmsnorm_quant(const uint16_t* input, uint16_t* resid
                                           float eps, int rows, int hidden, uint16_t* normed_out, uint8_t* out,
                                           float* scale_out, bool mn_major, hipStream_t stream);
 
+// The permutation's scratch: one int32 per (chunk of 1024 routing entries, expert).
+int64_t moe_permutation_scratch_ints(int64_t entries, int64_t num_experts);
 hipError_t launch_moe_build_permutation(const int32_t* topk_ids, int num_tokens, int top_k,
                                         int num_experts, int m_alloc, int32_t* m_indices,
-                                        int32_t* src_token, int32_t* row_of_entry,
+                                        int32_t* src_token, int32_t* row_of_entry, int32_t* hist,
                                         hipStream_t stream);
 hipError_t launch_moe_gather_quant(const uint16_t* x, const int32_t* src_token, int num_tokens,
                                    int hidden, int m_alloc, uint8_t* a_out, float* a_scale_out,
@@ -95,5 +100,8 @@ hipError_t launch_moe_silu_mul_quant(const uint16_t* y, const int32_t* m_indices
 hipError_t launch_moe_combine(const uint16_t* y, const int32_t* row_of_entry,
                               const float* topk_weights, int num_tokens, int top_k, int hidden,
                               int m_alloc, uint16_t* out, bool out_fp16, hipStream_t stream);
+
+// One wave spinning for spin_ticks of the wall clock; out[0] = shader-clock cycles, out[1] = wall ticks.
+hipError_t launch_clock_probe(unsigned long long* out, unsigned long long spin_ticks, hipStream_t stream);
 
 }  // namespace fp8g

@@ -15,10 +15,9 @@
 namespace fp8g {
 namespace kernels {
 
-constexpr int kPermThreads = 1024;  // 16 waves
+constexpr int kPermThreads = 1024;  // 16 waves; one routing entry per thread and chunk
 constexpr int kPermWaves = kPermThreads / 64;
 constexpr int kMaxExperts = 1024;
-constexpr int kPermBatch = 8;        // groups of 64 ids loaded together
 
 // Lanes of this wave whose (valid) id equals this lane's: one ballot per id bit. Valid ids are
 // below num_experts, so bits from `bits` = ceil(log2(num_experts)) up are zero in all of them.
@@ -31,59 +30,65 @@ __device__ __forceinline__ uint64_t match_id(int id, bool valid, int bits) {
   return m;
 }
 
-// Stable counting sort of the (token, slot) entries by expert. Workgroup c places the entries of
-// chunk c (kPermThreads entries, one group of 64 per wave). Every workgroup counts all entries per
-// expert -- in total, and before its chunk -- which gives the experts' 128-padded regions and the
-// chunk's first row inside each; within the chunk, the lanes holding the same expert find each
-// other with bit ballots (match_id), so an entry's row is its region start, plus the entries of
-// its expert in earlier chunks, in earlier groups of the chunk, and in earlier lanes. Entries keep
-// their order inside an expert, whatever the schedule. Workgroup 0 also writes the padding rows.
+__device__ __forceinline__ int id_bits_of(int num_experts) { return num_experts > 1 ? 32 - __clz(num_experts - 1) : 0; }
+
+// The permutation is a stable counting sort of the (token, slot) entries by expert, in three passes
+// over chunks of kPermThreads entries, with one int per (chunk, expert) in `hist`:
+//   1. histogram: chunk c's entry count per expert -> hist[c][e]; every row of m_indices and
+//      src_token is set to -1 (the padding value) on the way;
+//   2. scan (one workgroup): expert e owns rows [region_e, region_e + ceil(count_e/128)*128), in
+//      expert order; hist[c][e] becomes the first row of chunk c's entries of expert e, i.e. region_e
+//      plus the entries of e in earlier chunks;
+//   3. scatter: an entry's row is hist[c][e] plus the entries of its expert earlier in the chunk
+//      (earlier waves, from per-wave counts in LDS; earlier lanes, by matching ids with ballots).
+// Every pass is linear in the number of entries, and entries keep their order inside an expert.
+
 __global__ void __launch_bounds__(kPermThreads)
-moe_permutation_kernel(const int32_t* __restrict__ ids, int entries, int top_k, int num_experts,
-                       int m_alloc, int32_t* __restrict__ m_indices, int32_t* __restrict__ src_token,
-                       int32_t* __restrict__ row_of_entry) {
-  __shared__ int total_cnt[kMaxExperts];               // entries per expert
-  __shared__ int before_cnt[kMaxExperts];              // ... in earlier chunks
-  __shared__ int group_cnt[kPermWaves][kMaxExperts];   // ... in each group of this chunk
-  __shared__ int region[kMaxExperts + 1];              // first row of each region; [E]: rows used
-  __shared__ int scan_part[kPermWaves];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint64_t lanes_below = (1ull << lane) - 1;
-  const int chunk_begin = blockIdx.x * kPermThreads;
-  const int id_bits = num_experts > 1 ? 32 - __clz(num_experts - 1) : 0;  // wave-uniform
-
-  for (int i = tid; i < kMaxExperts; i += kPermThreads) total_cnt[i] = before_cnt[i] = 0;
-  for (int i = tid; i < kPermWaves * kMaxExperts; i += kPermThreads) (&group_cnt[0][0])[i] = 0;
-  __syncthreads();
-
-  // counts over all entries, kPermBatch groups of 64 per wave at a time so that the loads overlap
-  for (int g0 = wave * 64 * kPermBatch; g0 < entries; g0 += kPermThreads * kPermBatch) {
-    int idv[kPermBatch];
-#pragma unroll
-    for (int u = 0; u < kPermBatch; ++u) {
-      const int idx = g0 + u * 64 + lane;
-      idv[u] = idx < entries ? ids[idx] : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < kPermBatch; ++u) {
-      const int id = idv[u];
-      const bool valid = id >= 0 && id < num_experts;
-      const uint64_t same = match_id(id, valid, id_bits);
-      if (valid && (same >> lane) == 1) {  // the last lane holding this expert adds for all of them
-        atomicAdd(&total_cnt[id], __popcll(same));
-        if (g0 + u * 64 < chunk_begin) atomicAdd(&before_cnt[id], __popcll(same));  // groups never straddle
-      }
-    }
+moe_perm_histogram_kernel(const int32_t* __restrict__ ids, int entries, int num_experts, int chunks,
+                          int32_t* __restrict__ hist, int m_alloc, int32_t* __restrict__ m_indices,
+                          int32_t* __restrict__ src_token) {
+  __shared__ int cnt[kMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int r = blockIdx.x * kPermThreads + tid; r < m_alloc; r += gridDim.x * kPermThreads) {
+    m_indices[r] = -1;
+    src_token[r] = -1;
   }
-  const int idx = chunk_begin + wave * 64 + lane;  // this lane's entry of the chunk
+  if ((int)blockIdx.x >= chunks) return;  // uniform: the grid may be wider than the chunks
+  for (int e = tid; e < num_experts; e += kPermThreads) cnt[e] = 0;
+  __syncthreads();
+  const int idx = blockIdx.x * kPermThreads + tid;
   const int id = idx < entries ? ids[idx] : -1;
   const bool valid = id >= 0 && id < num_experts;
-  const uint64_t same = match_id(id, valid, id_bits);
-  if (valid && (same >> lane) == 1) group_cnt[wave][id] = __popcll(same);
+  const uint64_t same = match_id(id, valid, id_bits_of(num_experts));
+  if (valid && (same >> lane) == 1) atomicAdd(&cnt[id], __popcll(same));  // the last lane of each id adds for all
   __syncthreads();
+  int32_t* h = hist + (int64_t)blockIdx.x * num_experts;
+  for (int e = tid; e < num_experts; e += kPermThreads) h[e] = cnt[e];
+}
 
-  // regions: block-wide exclusive scan of the 128-padded counts, one thread per expert
-  const int count = tid < num_experts ? total_cnt[tid] : 0;
+// One workgroup. Thread t serves expert e = t % E and chunk slice s = t / E (E*S <= 1024 threads,
+// S = 1024 / E slices of consecutive chunks), so the reads of one chunk's row of hist are coalesced.
+__global__ void __launch_bounds__(kPermThreads)
+moe_perm_scan_kernel(int32_t* __restrict__ hist, int num_experts, int chunks) {
+  __shared__ int part[kPermThreads];     // [s][e]: entries of e in slice s
+  __shared__ int region[kMaxExperts];    // first row of e's region
+  __shared__ int scan_part[kPermWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = num_experts;
+  const int S = kPermThreads / E;
+  const int e = tid % E, s = tid / E;
+  const bool active = s < S;
+  const int per = (chunks + S - 1) / S;
+  const int c0 = min(s * per, chunks), c1 = min(c0 + per, chunks);
+  int sum = 0;
+  if (active)
+    for (int c = c0; c < c1; ++c) sum += hist[(int64_t)c * E + e];
+  if (active) part[s * E + e] = sum;
+  __syncthreads();
+  // 128-padded count of expert tid, and the block-wide exclusive scan of those counts
+  int count = 0;
+  if (tid < E)
+    for (int j = 0; j < S; ++j) count += part[j * E + tid];
   const int padded = (count + 127) & ~127;
   int incl = padded;
 #pragma unroll
@@ -95,31 +100,42 @@ moe_permutation_kernel(const int32_t* __restrict__ ids, int entries, int top_k, 
   __syncthreads();
   int before = 0;
   for (int w = 0; w < wave; ++w) before += scan_part[w];
-  const int start = before + incl - padded;
-  if (tid < num_experts) region[tid] = start;
-  if (tid == kPermThreads - 1) region[num_experts] = before + incl;
-  if (blockIdx.x == 0 && tid < num_experts) {
-    for (int r = start + count; r < start + padded; ++r) {  // the region's padding rows
-      m_indices[r] = -1;
-      src_token[r] = -1;
-    }
-  }
+  if (tid < E) region[tid] = before + incl - padded;
   __syncthreads();
+  if (!active) return;
+  int row = region[e];
+  for (int j = 0; j < s; ++j) row += part[j * E + e];
+  for (int c = c0; c < c1; ++c) {
+    int32_t* p = hist + (int64_t)c * E + e;
+    const int v = *p;
+    *p = row;
+    row += v;
+  }
+}
 
+__global__ void __launch_bounds__(kPermThreads)
+moe_perm_scatter_kernel(const int32_t* __restrict__ ids, int entries, int top_k, int num_experts,
+                        const int32_t* __restrict__ first_row, int32_t* __restrict__ m_indices,
+                        int32_t* __restrict__ src_token, int32_t* __restrict__ row_of_entry) {
+  __shared__ int wave_cnt[kPermWaves][kMaxExperts];  // entries of each expert in each wave
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = num_experts;
+  for (int i = tid; i < kPermWaves * E; i += kPermThreads) wave_cnt[i / E][i % E] = 0;
+  const int idx = blockIdx.x * kPermThreads + tid;
+  const int id = idx < entries ? ids[idx] : -1;
+  const bool valid = id >= 0 && id < E;
+  const uint64_t same = match_id(id, valid, id_bits_of(E));
+  __syncthreads();
+  if (valid && (same >> lane) == 1) wave_cnt[wave][id] = __popcll(same);
+  __syncthreads();
   if (valid) {
-    int row = region[id] + before_cnt[id] + __popcll(same & lanes_below);
-    for (int w = 0; w < wave; ++w) row += group_cnt[w][id];
+    int row = first_row[(int64_t)blockIdx.x * E + id] + __popcll(same & ((1ull << lane) - 1));
+    for (int w = 0; w < wave; ++w) row += wave_cnt[w][id];
     m_indices[row] = id;
     src_token[row] = idx / top_k;
     row_of_entry[idx] = row;
   } else if (idx < entries) {
     row_of_entry[idx] = -1;
-  }
-  if (blockIdx.x == 0) {
-    for (int r = region[num_experts] + tid; r < m_alloc; r += kPermThreads) {  // rows past every region
-      m_indices[r] = -1;
-      src_token[r] = -1;
-    }
   }
 }
 
@@ -204,13 +220,25 @@ moe_combine_kernel(const uint16_t* __restrict__ y, const int32_t* __restrict__ r
 
 using namespace kernels;
 
+int64_t moe_permutation_scratch_ints(int64_t entries, int64_t num_experts) {
+  return (entries + kPermThreads - 1) / kPermThreads * num_experts;
+}
+
 hipError_t launch_moe_build_permutation(const int32_t* topk_ids, int num_tokens, int top_k,
                                         int num_experts, int m_alloc, int32_t* m_indices,
-                                        int32_t* src_token, int32_t* row_of_entry,
+                                        int32_t* src_token, int32_t* row_of_entry, int32_t* hist,
                                         hipStream_t stream) {
-  const int chunks = std::max(1, (num_tokens * top_k + kPermThreads - 1) / kPermThreads);
-  hipLaunchKernelGGL(moe_permutation_kernel, dim3(chunks), dim3(kPermThreads), 0, stream, topk_ids,
-                     num_tokens * top_k, top_k, num_experts, m_alloc, m_indices, src_token, row_of_entry);
+  const int entries = num_tokens * top_k;
+  const int chunks = (entries + kPermThreads - 1) / kPermThreads;
+  const int fill_blocks = (m_alloc + kPermThreads - 1) / kPermThreads;
+  // one workgroup per chunk (every chunk needs its own), and enough for the fill's grid-stride loop
+  const int grid1 = std::max(1, std::max(chunks, std::min(fill_blocks, 4096)));
+  hipLaunchKernelGGL(moe_perm_histogram_kernel, dim3(grid1), dim3(kPermThreads), 0, stream, topk_ids, entries,
+                     num_experts, chunks, hist, m_alloc, m_indices, src_token);
+  if (chunks == 0) return hipGetLastError();
+  hipLaunchKernelGGL(moe_perm_scan_kernel, dim3(1), dim3(kPermThreads), 0, stream, hist, num_experts, chunks);
+  hipLaunchKernelGGL(moe_perm_scatter_kernel, dim3(chunks), dim3(kPermThreads), 0, stream, topk_ids, entries, top_k,
+                     num_experts, hist, m_indices, src_token, row_of_entry);
   return hipGetLastError();
 }
 

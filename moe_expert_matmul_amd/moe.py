@@ -6,7 +6,7 @@ first ``inter`` rows are the gate and the next ``inter`` the up projection, FP8 
 (E, hidden, inter), 128x128 FP32 block scales, and the top-k routing weights for the combine.
 
 Five library calls on the current stream, no host synchronisation:
-  permutation -> quantise the tokens -> fc1 grouped GEMM reading the token rows through the
+  permutation (three kernels) -> quantise the tokens -> fc1 grouped GEMM reading the token rows through the
   permutation, with SiLU-mul+quantise in its epilogue -> fc2 grouped GEMM -> combine
 (``fuse_activation=False`` runs fc1 and the activation as two calls, with the same result).
 """
@@ -35,6 +35,7 @@ class MoeWorkspace:
     m_indices: torch.Tensor
     src_token: torch.Tensor
     row_of_entry: torch.Tensor
+    perm_scratch: torch.Tensor  # the permutation's per-chunk expert counts
     a1: torch.Tensor  # the tokens, 1x128-quantised (num_tokens rows, in token order)
     sa1: torch.Tensor
     y1: torch.Tensor
@@ -50,6 +51,8 @@ class MoeWorkspace:
             m_indices=torch.empty(m_alloc, dtype=torch.int32, **e),
             src_token=torch.empty(m_alloc, dtype=torch.int32, **e),
             row_of_entry=torch.empty((num_tokens, top_k), dtype=torch.int32, **e),
+            perm_scratch=torch.empty(max(permutation_workspace_bytes(num_tokens, top_k, num_experts), 4),
+                                     dtype=torch.uint8, **e),
             a1=torch.empty((num_tokens, hidden), dtype=torch.uint8, **e),
             sa1=torch.empty((num_tokens, hidden // 128), dtype=torch.float32, **e),
             y1=torch.empty((m_alloc, 2 * inter), dtype=torch.bfloat16, **e),
@@ -63,7 +66,17 @@ class MoeWorkspace:
         return self.m_indices.shape[0]
 
 
-def moe_build_permutation(topk_ids, num_experts, m_indices, src_token, row_of_entry):
+def permutation_workspace_bytes(num_tokens: int, top_k: int, num_experts: int) -> int:
+    """Device scratch the permutation needs: one int32 per (chunk of 1024 routing entries, expert)."""
+    n = _lib.load().fp8_moe_permutation_workspace_size(num_tokens, top_k, num_experts)
+    if n < 0:
+        raise ValueError(f"invalid permutation sizes ({num_tokens}, {top_k}, {num_experts})")
+    return n
+
+
+def moe_build_permutation(topk_ids, num_experts, m_indices, src_token, row_of_entry, workspace=None):
+    """``workspace``: a uint8 device tensor of at least permutation_workspace_bytes(...) bytes (allocated
+    here when None)."""
     dev = _require_cuda(topk_ids)
     t, k = topk_ids.shape
     m_alloc = m_indices.shape[0]
@@ -71,10 +84,14 @@ def moe_build_permutation(topk_ids, num_experts, m_indices, src_token, row_of_en
     _check(m_indices, "m_indices", (torch.int32,), (m_alloc,), dev)
     _check(src_token, "src_token", (torch.int32,), (m_alloc,), dev)
     _check(row_of_entry, "row_of_entry", (torch.int32,), (t, k), dev)
+    if workspace is None:
+        workspace = torch.empty(max(permutation_workspace_bytes(t, k, num_experts), 4), dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace", (torch.uint8,), (workspace.numel(),), dev)
     with torch.cuda.device(dev):
         st = _lib.load().fp8_moe_build_permutation(topk_ids.data_ptr(), t, k, num_experts, m_alloc,
                                                    m_indices.data_ptr(), src_token.data_ptr(),
-                                                   row_of_entry.data_ptr(), _stream(dev))
+                                                   row_of_entry.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                                   _stream(dev))
     _lib.check(st, "fp8_moe_build_permutation")
 
 
@@ -171,7 +188,7 @@ def moe_ffn_fp8_block_scale(x, topk_ids, topk_weights, w1, s1, w2, s2, out=None,
     ws = workspace or MoeWorkspace.allocate(num_tokens, top_k, num_experts, hidden, inter, x.device)
     if out is None:
         out = torch.empty((num_tokens, hidden), dtype=torch.bfloat16, device=x.device)
-    moe_build_permutation(topk_ids, num_experts, ws.m_indices, ws.src_token, ws.row_of_entry)
+    moe_build_permutation(topk_ids, num_experts, ws.m_indices, ws.src_token, ws.row_of_entry, ws.perm_scratch)
     moe_gather_quant(x, None, ws.a1, ws.sa1)
     if fuse_activation:
         moe_fc1_silu_quant(ws.a1, ws.sa1, ws.src_token, w1, s1, ws.m_indices, ws.a2, ws.sa2)
@@ -193,6 +210,7 @@ class MoePerTensorWorkspace:
     m_indices: torch.Tensor
     src_token: torch.Tensor
     row_of_entry: torch.Tensor
+    perm_scratch: torch.Tensor  # the permutation's per-chunk expert counts
     a2: torch.Tensor  # fc2's E4M3 input, written by fc1's epilogue
     y2: torch.Tensor
 
@@ -204,6 +222,8 @@ class MoePerTensorWorkspace:
             m_indices=torch.empty(m_alloc, dtype=torch.int32, **e),
             src_token=torch.empty(m_alloc, dtype=torch.int32, **e),
             row_of_entry=torch.empty((num_tokens, top_k), dtype=torch.int32, **e),
+            perm_scratch=torch.empty(max(permutation_workspace_bytes(num_tokens, top_k, num_experts), 4),
+                                     dtype=torch.uint8, **e),
             a2=torch.empty((m_alloc, inter), dtype=torch.uint8, **e),
             y2=torch.empty((m_alloc, hidden), dtype=torch.bfloat16, **e),
         )
@@ -281,7 +301,7 @@ def moe_ffn_fp8_per_tensor(x_fp8, topk_ids, w1, w2, fc1_dequant, fc2_quant, fc2_
     ws = workspace or MoePerTensorWorkspace.allocate(num_tokens, top_k, num_experts, hidden, inter, x_fp8.device)
     if out is None:
         out = torch.empty((num_tokens, hidden), dtype=out_dtype, device=x_fp8.device)
-    moe_build_permutation(topk_ids, num_experts, ws.m_indices, ws.src_token, ws.row_of_entry)
+    moe_build_permutation(topk_ids, num_experts, ws.m_indices, ws.src_token, ws.row_of_entry, ws.perm_scratch)
     moe_fc1_silu_quant_per_tensor(x_fp8, ws.src_token, w1, fc1_dequant, fc2_quant, ws.m_indices, ws.a2)
     fp8_group_gemm_contiguous_per_tensor(ws.a2, None, w2, fc2_dequant, ws.m_indices, ws.y2)
     moe_combine(ws.y2, ws.row_of_entry, topk_weights, out)

@@ -125,8 +125,15 @@ def test_masked_rejects_negative_expected_m(lib):
 
 def test_moe_steps_validate_sizes(lib):
     # m_alloc too small for 4 tokens x 2 slots over 3 experts (needs 128 * ceil((8 + 381) / 128) = 512)
-    st, msg = _status(lib.fp8_moe_build_permutation, P, 4, 2, 3, 256, P, P, P, None)
+    st, msg = _status(lib.fp8_moe_build_permutation, P, 4, 2, 3, 256, P, P, P, P, 1 << 20, None)
     assert st == _lib.INVALID_ARGUMENT and "m_alloc" in msg
+    # the workspace holds one int32 per (chunk of 1024 entries, expert)
+    assert lib.fp8_moe_permutation_workspace_size(4, 2, 3) == 12
+    assert lib.fp8_moe_permutation_workspace_size(4096, 8, 64) == 32 * 64 * 4
+    assert lib.fp8_moe_permutation_workspace_size(0, 8, 64) == 0
+    assert lib.fp8_moe_permutation_workspace_size(4, 2, 1025) == -1
+    st, msg = _status(lib.fp8_moe_build_permutation, P, 4, 2, 3, 512, P, P, P, P, 11, None)
+    assert st == _lib.INVALID_ARGUMENT and "workspace" in msg
     st, _ = _status(lib.fp8_moe_gather_quant, P, P, 4, 100, 128, P, P, None)
     assert st == _lib.INVALID_ARGUMENT
     st, _ = _status(lib.fp8_moe_silu_mul_quant, P, P, 128, 100, P, P, None)
