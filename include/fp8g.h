@@ -8,7 +8,8 @@
  * README, section "Additional Notes"):
  *   - Memory is owned by the caller. Every pointer argument is a DEVICE pointer on the current HIP
  *     device unless it is documented otherwise. The library never allocates, frees or keeps a
- *     pointer after the call returns.
+ *     pointer after the call returns; scratch space comes in as a workspace argument, except for
+ *     fp8_moe_build_permutation_noalloc, which uses a fixed array of the library's own.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the call returns
  *     without synchronising. No call reads device memory from the host.
  *   - Arguments are validated before anything is launched; C++ exceptions never cross the ABI. A
@@ -267,6 +268,22 @@ FP8G_API fp8g_status_t fp8_moe_build_permutation(const int32_t* topk_ids, int64_
                                         int32_t* m_indices, int32_t* src_token,
                                         int32_t* row_of_entry, void* workspace, int64_t workspace_bytes,
                                         void* stream);
+
+/*
+ * fp8_moe_build_permutation without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Same
+ * arguments, result and errors as fp8_moe_build_permutation, except that the per-chunk counts live in
+ * the library's own device array of 4 MiB (1048576 int32), one copy per device, held until the process
+ * ends. Sizes whose counts do not fit -- ceil(num_tokens*top_k / 1024) * num_experts > 1048576, e.g.
+ * more than 16.7 M entries over 64 experts or 1 M entries over 1024 experts -- return
+ * FP8G_INVALID_ARGUMENT. The call allocates nothing and needs no initialisation of the array (every
+ * count it reads is written earlier in the same call). Calls that overlap on one device (on different
+ * streams, or from different threads, before the previous one has finished) share that array and race.
+ */
+FP8G_API fp8g_status_t fp8_moe_build_permutation_noalloc(const int32_t* topk_ids, int64_t num_tokens,
+                                                         int64_t top_k, int64_t num_experts, int64_t m_alloc,
+                                                         int32_t* m_indices, int32_t* src_token,
+                                                         int32_t* row_of_entry, void* stream);
 
 /*
  * Quantise BF16 token rows per 1x128 block into the permuted layout:

@@ -23,6 +23,7 @@ from .moe import (  # noqa: F401
     MoeWorkspace,
     default_m_alloc,
     moe_build_permutation,
+    moe_build_permutation_noalloc,
     fp8_group_gemm_contiguous_per_tensor,
     moe_combine,
     moe_fc1_silu_quant,

@@ -40,6 +40,7 @@ SIGNATURES = {
     "fp8_fused_add_rmsnorm_quant": ([_P, _P, _P, _P, _P, _P, ctypes.c_float, _I64, _I64, _I32, _P], _I32),
     "fp8_moe_permutation_workspace_size": ([_I64, _I64, _I64], _I64),
     "fp8_moe_build_permutation": ([_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _I64, _P], _I32),
+    "fp8_moe_build_permutation_noalloc": ([_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P], _I32),
     "fp8_moe_gather_quant": ([_P, _P, _I64, _I64, _I64, _P, _P, _P], _I32),
     "fp8_moe_silu_mul_quant": ([_P, _P, _I64, _I64, _P, _P, _P], _I32),
     "fp8_moe_fc1_silu_quant": ([_P, _P, _I64, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32,

@@ -560,6 +560,30 @@ fp8g_status_t fp8_moe_build_permutation(const int32_t* topk_ids, int64_t num_tok
   });
 }
 
+fp8g_status_t fp8_moe_build_permutation_noalloc(const int32_t* topk_ids, int64_t num_tokens, int64_t top_k,
+                                                int64_t num_experts, int64_t m_alloc, int32_t* m_indices,
+                                                int32_t* src_token, int32_t* row_of_entry, void* stream) {
+  return guarded([&] {
+    if (!check_permutation(topk_ids, num_tokens, top_k, num_experts, m_alloc, m_indices, src_token, row_of_entry))
+      return;
+    const int64_t need = fp8g::moe_permutation_scratch_ints(num_tokens * top_k, num_experts);
+    require(need <= fp8g::kPermScratchInts,
+            "num_tokens*top_k (%lld) over num_experts (%lld) needs %lld scratch ints; the library's own scratch "
+            "holds %lld (ceil(num_tokens*top_k/1024)*num_experts must not exceed it)",
+            (long long)(num_tokens * top_k), (long long)num_experts, (long long)need,
+            (long long)fp8g::kPermScratchInts);
+    check_device();
+    int dev = 0;
+    check_hip(hipGetDevice(&dev), "hipGetDevice");
+    int32_t* hist = nullptr;
+    check_hip(fp8g::permutation_scratch(dev, &hist), "looking up the permutation scratch");
+    check_hip(fp8g::launch_moe_build_permutation(topk_ids, (int)num_tokens, (int)top_k, (int)num_experts,
+                                                 (int)m_alloc, m_indices, src_token, row_of_entry, hist,
+                                                 (hipStream_t)stream),
+              "fp8_moe_build_permutation_noalloc launch");
+  });
+}
+
 fp8g_status_t fp8_moe_gather_quant(const void* x, const int32_t* src_token, int64_t num_tokens,
                                    int64_t hidden, int64_t m_alloc, void* a_out,
                                    float* a_scale_out, void* stream) {

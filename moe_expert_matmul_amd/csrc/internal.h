@@ -87,6 +87,11 @@ hipError_t launch_fused_add_rmsnorm_quant(const uint16_t* input, uint16_t* resid
 
 // The permutation's scratch: one int32 per (chunk of 1024 routing entries, expert).
 int64_t moe_permutation_scratch_ints(int64_t entries, int64_t num_experts);
+// The library's own permutation scratch (a device array of kPermScratchInts int32, one copy per
+// device, held until the process ends), for callers that cannot allocate; `device` must be current.
+constexpr int64_t kPermScratchInts = 1 << 20;  // 4 MiB
+constexpr int kMaxScratchDevices = 64;
+hipError_t permutation_scratch(int device, int32_t** ptr);
 hipError_t launch_moe_build_permutation(const int32_t* topk_ids, int num_tokens, int top_k,
                                         int num_experts, int m_alloc, int32_t* m_indices,
                                         int32_t* src_token, int32_t* row_of_entry, int32_t* hist,

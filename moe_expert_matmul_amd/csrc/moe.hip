@@ -8,6 +8,7 @@
 // block is handled by 16 lanes holding 8 consecutive elements (16-byte loads), and its amax is a
 // 16-lane butterfly reduction.
 #include <algorithm>
+#include <mutex>
 
 #include "internal.h"
 #include "quant_common.h"
@@ -219,6 +220,31 @@ moe_combine_kernel(const uint16_t* __restrict__ y, const int32_t* __restrict__ r
 }  // namespace kernels
 
 using namespace kernels;
+
+// Scratch of the allocation-free permutation (fp8_moe_build_permutation_noalloc): the per-chunk
+// expert counts, one int32 per (chunk of 1024 entries, expert), at most kPermScratchInts of them. Each
+// device holds its own copy for the life of the process. Host code must not pass `scratch` itself to
+// a kernel (the name is a host-side stand-in there); it uses the device address looked up below.
+static __device__ __align__(256) int32_t scratch[kPermScratchInts];
+
+namespace {
+std::mutex g_scratch_mutex;
+int32_t* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t permutation_scratch(int device, int32_t** ptr) {
+  if (device < 0 || device >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[device] == nullptr) {
+    void* p = nullptr;
+    // with `device` current (the caller's current device): this device's copy of the array
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[device] = static_cast<int32_t*>(p);
+  }
+  *ptr = g_scratch_ptr[device];
+  return hipSuccess;
+}
 
 int64_t moe_permutation_scratch_ints(int64_t entries, int64_t num_experts) {
   return (entries + kPermThreads - 1) / kPermThreads * num_experts;

@@ -95,6 +95,23 @@ def moe_build_permutation(topk_ids, num_experts, m_indices, src_token, row_of_en
     _lib.check(st, "fp8_moe_build_permutation")
 
 
+def moe_build_permutation_noalloc(topk_ids, num_experts, m_indices, src_token, row_of_entry):
+    """moe_build_permutation with the library's own scratch (no workspace, nothing allocated); calls
+    that overlap on one device race on that scratch."""
+    dev = _require_cuda(topk_ids)
+    t, k = topk_ids.shape
+    m_alloc = m_indices.shape[0]
+    _check(topk_ids, "topk_ids", (torch.int32,), (t, k), dev)
+    _check(m_indices, "m_indices", (torch.int32,), (m_alloc,), dev)
+    _check(src_token, "src_token", (torch.int32,), (m_alloc,), dev)
+    _check(row_of_entry, "row_of_entry", (torch.int32,), (t, k), dev)
+    with torch.cuda.device(dev):
+        st = _lib.load().fp8_moe_build_permutation_noalloc(topk_ids.data_ptr(), t, k, num_experts, m_alloc,
+                                                           m_indices.data_ptr(), src_token.data_ptr(),
+                                                           row_of_entry.data_ptr(), _stream(dev))
+    _lib.check(st, "fp8_moe_build_permutation_noalloc")
+
+
 def moe_gather_quant(x, src_token, a_out, a_scale_out):
     """Row r of a_out/a_scale_out: x[src_token[r]] quantised per 1x128 block (rows with -1 untouched).
 
