@@ -8,9 +8,11 @@ timed with HIP events on the stream the kernel is launched on; an event between 
 per-launch median and minimum beside the mean. value = algorithmic TFLOP/s (2*m*n*k per launch).
 ``roofline`` prices that against the dense FP8 matrix-core peak; ``traffic`` comes from the committed
 rocprofv3 FETCH_SIZE/WRITE_SIZE summary when it was taken on the current kernel source, else null.
-``sclk_mhz`` is the shader clock read by a one-wave probe enqueued right after the timed launches
-(the clock the part settled at under that load); ``frac_at_sclk`` prices the same time against the
-peak at that clock. ``cpu_baseline`` times the float64 CPU oracle on a bounded row sample.
+``sclk_mhz`` is the shader clock the last timed launch ran at (from the clock stamps the kernel's first
+workgroup writes); ``frac_at_sclk`` prices the same time against the peak at that clock. The
+part is held at its board power limit under this load, which sets that clock.
+``sclk_after_timed_region_mhz`` is a one-wave probe right after the region (the clock recovers at
+once, so it reads higher). ``cpu_baseline`` times the float64 CPU oracle on a bounded row sample.
 
 ``configs`` holds every workload of the benchmark, each with median and minimum per-launch time,
 algorithmic TFLOP/s, the fraction of its binding roofline, and the SHA-256 of its generated inputs:
@@ -93,6 +95,18 @@ def sclk_probe(spin_us: int = 200):
         khz = lib.fp8g_wall_clock_khz()
         return round(cycles / ticks * khz / 1000.0, 1) if ticks > 0 and khz > 0 else None
     return read
+
+
+def gemm_clock_mhz():
+    """Average shader clock of the most recent GEMM launch, from the stamps its first workgroup wrote."""
+    import ctypes
+    from moe_expert_matmul_amd import _lib
+    lib = _lib.load()
+    st = (ctypes.c_ulonglong * 4)()
+    _lib.check(lib.fp8g_gemm_clock_record(st), "fp8g_gemm_clock_record")
+    khz = lib.fp8g_wall_clock_khz()
+    ticks = st[3] - st[1]
+    return round((st[2] - st[0]) / ticks * khz / 1000.0, 1) if ticks > 0 and khz > 0 else None
 
 
 def time_launches(fn, steps: int, warmup: int, probe: bool = False):
@@ -211,7 +225,7 @@ def benchmark_configs(headline, steps, warmup):
     _, med, best, _, _ = time_launches(fn, max(steps, 20), warmup)
     e = roofline_entry(med, best, 2.0 * 128 * 256 * 512, 128 * 512 + 256 * 512 + 4 * (128 * 4 + 2 * 4) + 2 * 128 * 256)
     e["bound"] = "launch latency (parity-size case)"
-    res["1_plain_m128_n256_k512"] = dict(e, timing="back to back", inputs_sha256=inputs_sha256(
+    res["1_plain_m128_n256_k512"] = dict(e, timing="back to back", sclk_mhz=gemm_clock_mhz(), inputs_sha256=inputs_sha256(
         d["a"], d["b"], d["a_scale"], d["b_scale"]))
     del d, out
 
@@ -230,7 +244,8 @@ def benchmark_configs(headline, steps, warmup):
     hbm = d["a"].numel() + d["b"].numel() + 4 * (d["a_scale"].numel() + d["b_scale"].numel()) + d["m"] * 4 \
         + 2 * valid * 4096
     res["3_contiguous_32experts_zipf_8192rows_n4096_k7168"] = dict(
-        roofline_entry(med, best, 2.0 * valid * 4096 * 7168, hbm), timing="cold caches", m_pad=d["m"],
+        roofline_entry(med, best, 2.0 * valid * 4096 * 7168, hbm), timing="cold caches", sclk_mhz=gemm_clock_mhz(),
+        m_pad=d["m"],
         valid_rows=valid, inputs_sha256=inputs_sha256(d["a"], d["b"], d["a_scale"], d["b_scale"], d["m_indices"]))
     del d, out
 
@@ -243,7 +258,8 @@ def benchmark_configs(headline, steps, warmup):
     rows = int(mm.sum())
     hbm = rows * 7168 + live * 4096 * 7168 + 2 * rows * 4096 + 4 * (rows * 56 + live * 32 * 56) + 16 * 4
     res["4_masked_16groups_maxm256_n4096_k7168"] = dict(
-        roofline_entry(med, best, 2.0 * rows * 4096 * 7168, hbm), timing="cold caches", sum_masked_m=rows,
+        roofline_entry(med, best, 2.0 * rows * 4096 * 7168, hbm), timing="cold caches", sclk_mhz=gemm_clock_mhz(),
+        sum_masked_m=rows,
         inputs_sha256=inputs_sha256(d["a"], d["b"], d["a_scale"], d["b_scale"], d["masked_m"]))
     del d, out
 
@@ -258,6 +274,7 @@ def benchmark_configs(headline, steps, warmup):
     bound = ffn_stage_roofline_us(rows, 4096, 7168, 2048, 64, 8)
     res["5_moe_ffn_4096tok_h7168_e64_top8_i2048"] = dict(
         roofline_entry(med, best, flops, 0.0, bound_us=bound), timing="cold caches", routed_rows=rows,
+        sclk_mhz_fc2=gemm_clock_mhz(),
         note="roofline_us sums max(MFMA, HBM) time over the chain's kernels; tflops counts fc1 + fc2",
         inputs_sha256=inputs_sha256(d["x"], d["topk_ids"], d["topk_weights"], d["w1"], d["s1"], d["w2"], d["s2"]))
     del d, ws, out, scratch
@@ -390,12 +407,13 @@ def main():
     idle_clock = sclk_probe()
     torch.cuda.synchronize()
     idle_mhz = idle_clock()
-    ms, med, best, wall, sclk = time_launches(fn, args.steps, args.warmup, probe=True)
+    ms, med, best, wall, sclk_after = time_launches(fn, args.steps, args.warmup, probe=True)
+    sclk = gemm_clock_mhz()  # the clock the last timed launch ran at
     flops = 2.0 * m * n * k
     tflops = flops / ms / 1e9
     frac = tflops / FP8_DENSE_PEAK_TFLOPS
     headline = dict(roofline_entry(med, best, flops, m * k + n * k + 4 * (m * 56 + 32 * 56) + 2 * m * n),
-                    us_mean=round(ms * 1e3, 2), timing="back to back",
+                    us_mean=round(ms * 1e3, 2), timing="back to back", sclk_mhz=sclk,
                     inputs_sha256=inputs_sha256(d["a"], d["b"], d["a_scale"], d["b_scale"]))
     line = {
         "metric": "FP8 groupwise GEMM TFLOP/s and % of MI355X dense-FP8 MFMA peak",
@@ -417,6 +435,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": FP8_DENSE_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(frac, 4), "traffic": load_traffic()},
         "sclk_mhz": sclk,
+        "sclk_after_timed_region_mhz": sclk_after,
         "sclk_idle_mhz": idle_mhz,
         "frac_at_sclk": round(frac * NOMINAL_SCLK_MHZ / sclk, 4) if sclk else None,
         "wall_s_timed_region": round(wall, 4),

@@ -84,6 +84,17 @@ FP8G_API int32_t fp8g_version(void);
  */
 FP8G_API fp8g_status_t fp8g_clock_probe(unsigned long long* out, int64_t spin_us, void* stream);
 
+/*
+ * Measurement aid (not part of the method): the clock the most recent GEMM launch on the current
+ * device ran at. Every GEMM kernel's first workgroup stamps the shader-clock counter and the
+ * constant-rate wall clock when it starts and when it leaves; this copies the four stamps (start
+ * cycles, start ticks, end cycles, end ticks) to host_out (HOST memory, four uint64). The average
+ * shader clock in kHz is (end cycles - start cycles) / (end ticks - start ticks) * fp8g_wall_clock_khz().
+ * Synchronous (a device-to-host copy); launches overlapping on several streams overwrite each other's
+ * stamps.
+ */
+FP8G_API fp8g_status_t fp8g_gemm_clock_record(unsigned long long* host_out);
+
 /* Rate of the current device's wall clock (hipDeviceAttributeWallClockRate) in kHz; -1 on error. */
 FP8G_API int64_t fp8g_wall_clock_khz(void);
 

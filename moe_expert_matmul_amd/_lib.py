@@ -25,6 +25,7 @@ SIGNATURES = {
     "fp8g_last_error": ([], ctypes.c_char_p),
     "fp8g_version": ([], _I32),
     "fp8g_clock_probe": ([_P, _I64, _P], _I32),
+    "fp8g_gemm_clock_record": ([_P], _I32),
     "fp8g_wall_clock_khz": ([], _I64),
     "fp8_gemm_nt_groupwise": ([_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P], _I32),
     "fp8_gemm_nt_groupwise_fp8_out": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P], _I32),

@@ -204,6 +204,14 @@ fp8g_status_t fp8g_clock_probe(unsigned long long* out, int64_t spin_us, void* s
   });
 }
 
+fp8g_status_t fp8g_gemm_clock_record(unsigned long long* host_out) {
+  return guarded([&] {
+    require(host_out != nullptr, "host_out must be non-null");
+    check_device();
+    check_hip(fp8g::gemm_clock_record(host_out), "fp8g_gemm_clock_record");
+  });
+}
+
 int64_t fp8g_wall_clock_khz(void) {
   int dev = 0, khz = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;

@@ -54,6 +54,10 @@ namespace kernels {
 constexpr int LOAD_GROUPS = 4;
 constexpr int LOAD_GROUPS_DEFER = 6;
 constexpr int BPRE = 1;  // measured against 2 and 3: the expert FFN 1.5% faster, the plain form level
+#ifndef FP8G_LDS_EPILOGUE
+#define FP8G_LDS_EPILOGUE 1
+#endif
+constexpr bool LDS_EPILOGUE = FP8G_LDS_EPILOGUE;
 
 template <int BM, int BN, int WM, int WN, int STAGES>
 struct Tile {
@@ -190,9 +194,36 @@ __device__ __forceinline__ void swiglu_pt_epilogue(const GemmParams& p, const f3
   }
 }
 
+// Measurement aid: the shader-clock and wall-clock stamps of the first workgroup of the most recent
+// GEMM launch (start cycles, start ticks, end cycles, end ticks); fp8g_gemm_clock_record reads them.
+__device__ unsigned long long g_gemm_clock[4];
+
+// Writes the first workgroup's end stamps when it leaves the kernel, on every return path.
+struct ClockStamp {
+  unsigned long long c0 = 0, w0 = 0;
+  bool on = false;
+  __device__ ClockStamp() {
+    on = blockIdx.x == 0 && __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;  // wave 0: uniform
+    if (on) {
+      c0 = clock64();
+      w0 = wall_clock64();
+    }
+  }
+  __device__ ~ClockStamp() {
+    if (on && threadIdx.x == 0) {
+      const unsigned long long c1 = clock64(), w1 = wall_clock64();
+      g_gemm_clock[0] = c0;
+      g_gemm_clock[1] = w0;
+      g_gemm_clock[2] = c1;
+      g_gemm_clock[3] = w1;
+    }
+  }
+};
+
 template <int BM, int BN, int WM, int WN, int STAGES, int MODE>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_fp8_groupwise_kernel(const GemmParams p) {
+  const ClockStamp stamp;
   using T = Tile<BM, BN, WM, WN, STAGES>;
   constexpr bool PT = MODE == MODE_CONTIG_PT || MODE == MODE_CONTIG_PT_SWIGLU;
   constexpr bool CONTIG = MODE == MODE_CONTIG || MODE == MODE_CONTIG_SWIGLU || PT;
@@ -663,6 +694,67 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     return;
   }
 
+  // ---- epilogue through LDS (plain, masked and contiguous forms, 16-bit output, all of the tile's
+  // columns in range, n a multiple of 8): the waves write their rounded values into the now idle
+  // stages as a BMxBN row-major tile, then every wave stores whole rows, 16 bytes per lane, so each
+  // store instruction writes two (BN = 256) or four (BN = 128) complete 2*BN-byte row segments
+  // instead of 16 rows x 32 bytes. In LDS the 8-byte unit c of tile row r sits at unit
+  // c ^ (2 * (r & 15)): the 16 rows a fragment lane group writes land on distinct banks, and a lane's
+  // two units of a 16-byte read stay adjacent. The contiguous form's row validity (the row's expert
+  // is this tile's, and its half is covered here) travels as one byte per row after the tile.
+  constexpr bool LDS_EPI_MODE = MODE == MODE_PLAIN || MODE == MODE_MASKED || MODE == MODE_CONTIG ||
+                                MODE == MODE_CONTIG_PT;
+  if constexpr (LDS_EPILOGUE && LDS_EPI_MODE) {
+    static_assert(BM * BN * 2 + BM <= STAGES * T::STAGE_BYTES, "the output tile and its row flags fit in the stages");
+    if (p.out_scale == nullptr && (p.n & 7) == 0 && col0 + BN <= p.n) {  // uniform
+      constexpr int PITCH = BN * 2;  // bytes per tile row
+      uint8_t* row_flag = smem + BM * BN * 2;
+      lds_pipeline_barrier();        // every wave has finished reading the stages
+      if constexpr (CONTIG) {
+        // the first wave of each row block: one flag per row of the block (lane l: row i0 + l)
+        if (wave % WN == 0)
+          row_flag[i0 + lane] = (wave_live && wave_ids == bsel && row0 + i0 + lane < row_end) ? 1 : 0;
+      }
+      if (wave_live) {
+        const int jl = (lane >> 4) * 4;
+        const float d = PT ? pt_dequant : 1.0f;
+#pragma unroll
+        for (int ig = 0; ig < T::IG; ++ig) {
+          const int r = i0 + ig * 16 + fr;
+#pragma unroll
+          for (int jg = 0; jg < T::JG; ++jg) {
+            const int c = (j0 + jg * 16 + jl) >> 2;  // 8-byte unit of the row
+            f32x4 a = acc[ig][jg];
+            if constexpr (PT) a *= d;
+            uint2 v;
+            if (p.out_fp16) {
+              v.x = __builtin_bit_cast(uint32_t, f16x2{(_Float16)a[0], (_Float16)a[1]});
+              v.y = __builtin_bit_cast(uint32_t, f16x2{(_Float16)a[2], (_Float16)a[3]});
+            } else {
+              v.x = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a[0], (__bf16)a[1]});
+              v.y = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a[2], (__bf16)a[3]});
+            }
+            *reinterpret_cast<uint2*>(smem + r * PITCH + ((c ^ (2 * (r & 15))) << 3)) = v;
+          }
+        }
+      }
+      lds_pipeline_barrier();
+      constexpr int LANES_PER_ROW = PITCH / 16;
+      constexpr int ROWS_PER_STORE = 64 / LANES_PER_ROW;
+      constexpr int ROWS_PER_WAVE = BM / T::NWAVES;
+      const int u = 2 * (lane % LANES_PER_ROW);  // first 8-byte unit of this lane's 16 bytes
+      uint16_t* O = p.out + (int64_t)g * p.out_group_stride;
+#pragma unroll
+      for (int s0 = 0; s0 < ROWS_PER_WAVE; s0 += ROWS_PER_STORE) {
+        const int r = wave * ROWS_PER_WAVE + s0 + lane / LANES_PER_ROW;
+        const uint4 v = *reinterpret_cast<const uint4*>(smem + r * PITCH + ((u ^ (2 * (r & 15))) << 3));
+        const bool ok = CONTIG ? row_flag[r] != 0 : row0 + r < row_end;
+        if (ok) *reinterpret_cast<uint4*>(O + (int64_t)(row0 + r) * p.n + col0 + 4 * u) = v;
+      }
+      return;
+    }
+  }
+
   // ---- epilogue: BF16 or FP16 round-to-nearest-even (8-byte stores), or E4M3 codes (4-byte
   // stores) when the plain form has an output scale; valid rows and columns only. A lane holds 4
   // consecutive columns; when n is not a multiple of 4 the row starts lose that alignment and each
@@ -858,6 +950,10 @@ using namespace kernels;
 int tile_rows(TileConfig cfg) { return (cfg == TILE_128x256 || cfg == TILE_128x128) ? 128 : 256; }
 int tile_cols(TileConfig cfg) {
   return (cfg == TILE_256x128 || cfg == TILE_128x128) ? 128 : 256;
+}
+
+hipError_t gemm_clock_record(unsigned long long* host4) {
+  return hipMemcpyFromSymbol(host4, HIP_SYMBOL(kernels::g_gemm_clock), 4 * sizeof(unsigned long long));
 }
 
 hipError_t launch_gemm(GemmMode mode, TileConfig cfg, GemmParams p, int grid, hipStream_t stream) {

@@ -106,6 +106,9 @@ hipError_t launch_moe_combine(const uint16_t* y, const int32_t* row_of_entry,
                               const float* topk_weights, int num_tokens, int top_k, int hidden,
                               int m_alloc, uint16_t* out, bool out_fp16, hipStream_t stream);
 
+// Stamps of the first workgroup of the most recent GEMM launch on the current device (start cycles,
+// start wall ticks, end cycles, end wall ticks), copied to host memory; synchronous.
+hipError_t gemm_clock_record(unsigned long long* host4);
 // One wave spinning for spin_ticks of the wall clock; out[0] = shader-clock cycles, out[1] = wall ticks.
 hipError_t launch_clock_probe(unsigned long long* out, unsigned long long spin_ticks, hipStream_t stream);
 
