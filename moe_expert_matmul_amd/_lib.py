@@ -69,6 +69,22 @@ class Fp8gInvalidArgument(Fp8gError, ValueError):
 
 
 _lib = None
+POISON_LIB_PATH = os.path.join(_PKG_DIR, "libfp8g_poison_lds.so")
+
+
+def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
+    for name, (argtypes, restype) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = argtypes
+        fn.restype = restype
+    return lib
+
+
+def load_poison_lds() -> ctypes.CDLL:
+    """The debug build whose GEMM kernels start with NaN-poisoned LDS (for the pipeline tests)."""
+    if not os.path.exists(POISON_LIB_PATH):
+        raise ImportError(f"{POISON_LIB_PATH} is missing: build with `python -m moe_expert_matmul_amd.build`")
+    return _bind(ctypes.CDLL(POISON_LIB_PATH))
 
 
 def load() -> ctypes.CDLL:
@@ -78,12 +94,7 @@ def load() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with `python -m moe_expert_matmul_amd.build` "
                               "(the HIP library is the only implementation)")
-        lib = ctypes.CDLL(LIB_PATH)
-        for name, (argtypes, restype) in SIGNATURES.items():
-            fn = getattr(lib, name)
-            fn.argtypes = argtypes
-            fn.restype = restype
-        _lib = lib
+        _lib = _bind(ctypes.CDLL(LIB_PATH))
     return _lib
 
 

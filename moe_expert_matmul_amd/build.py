@@ -20,6 +20,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libfp8g.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+POISON_LIB_PATH = os.path.join(PKG_DIR, "libfp8g_poison_lds.so")  # debug build, NaN-poisoned LDS
 SOURCES = ["api.hip", "gemm.hip", "moe.hip", "quant.hip", "bmm.hip", "clock.hip"]
 
 ARCH = "gfx950"
@@ -65,7 +66,40 @@ def build(verbose: bool = False) -> str:
     tmp = LIB_PATH + ".tmp"
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
     os.replace(tmp, LIB_PATH)
+    # debug build: the GEMM kernels start with NaN-poisoned LDS (the other objects are shared)
+    poison_obj = os.path.join(BUILD_DIR, "gemm_poison.o")
+    _run([hipcc, *COMMON_FLAGS, *DEVICE_FLAGS, "-DFP8G_POISON_LDS=1", "-c", os.path.join(CSRC, "gemm.hip"), "-o",
+          poison_obj])
+    others = [o for o in objs if os.path.basename(o) != "gemm.o"]
+    tmp = POISON_LIB_PATH + ".tmp"
+    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", poison_obj, *others, "-o", tmp])
+    os.replace(tmp, POISON_LIB_PATH)
     return LIB_PATH
+
+
+# Host code instrumented with AddressSanitizer and UndefinedBehaviorSanitizer; device code untouched
+# (each -fsanitize= applies to the host pass only). The library is linked without a sanitizer
+# runtime: the program that loads it must be built with the same sanitizers, which provides one.
+HOST_SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                       "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def build_host_sanitized(out_dir: str) -> str:
+    """Compile every source with host-side ASan and UBSan into out_dir/libfp8g.so (for CPU tests of
+    the validation layer); returns its path."""
+    hipcc = _hipcc()
+    os.makedirs(out_dir, exist_ok=True)
+    objs, jobs = [], []
+    for src in SOURCES:
+        obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        jobs.append([hipcc, *COMMON_FLAGS, *DEVICE_FLAGS, *HOST_SANITIZE_FLAGS, "-c", os.path.join(CSRC, src),
+                     "-o", obj])
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as ex:
+        list(ex.map(_run, jobs))
+    lib = os.path.join(out_dir, LIB_NAME)
+    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", lib])
+    return lib
 
 
 if __name__ == "__main__":

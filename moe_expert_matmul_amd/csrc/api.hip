@@ -145,7 +145,21 @@ void set_scale_strides(fp8g::GemmParams& p, int32_t scale_major, int64_t rows) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// a * b for non-negative sizes, saturated at INT64_MAX instead of overflowing (validation compares
+// products of caller-supplied sizes against limits before anything is narrowed).
+int64_t mul_sat(int64_t a, int64_t b) {
+  int64_t r;
+  return __builtin_mul_overflow(a, b, &r) ? INT64_MAX : r;
+}
+
 }  // namespace
+
+int fp8g::group_m_override(int group_m) {
+  const char* e = std::getenv("FP8G_GROUP_M");
+  if (!e) return group_m;
+  const int v = std::atoi(e);
+  return v > 0 ? v : group_m;
+}
 
 int fp8g::tile_override() {
   const char* e = std::getenv("FP8G_TILE");
@@ -235,7 +249,6 @@ void plain_gemm(const void* a, const void* b, const float* a_scale, const float*
   if (out_scale == nullptr) check_out_dtype(out_dtype);
   if (m == 0 || n == 0) return;
   check_operands(a, b, a_scale, b_scale, out, k);
-  check_device();
   fp8g::GemmParams p{};
   p.a = static_cast<const uint8_t*>(a);
   p.b = static_cast<const uint8_t*>(b);
@@ -256,8 +269,10 @@ void plain_gemm(const void* a, const void* b, const float* a_scale, const float*
   if (fp8g::tile_override() >= 0) cfg = (fp8g::TileConfig)fp8g::tile_override();
   p.tiles_m = (int32_t)ceil_div(m, fp8g::tile_rows(cfg));
   p.tiles_n = (int32_t)ceil_div(n, fp8g::tile_cols(cfg));
-  p.group_m = 4;
-  const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
+  p.group_m = fp8g::group_m_override(4);
+  const int64_t grid = mul_sat(p.tiles_m, p.tiles_n);
+  require(grid <= kInt32Max, "too many tiles");
+  check_device();
   launch_logged(what, fp8g::MODE_PLAIN, cfg, p, grid, stream);
 }
 
@@ -373,8 +388,8 @@ void group_gemm_contiguous(const void* a, const float* a_scale, int64_t a_src_ro
   // 128-row tiles: the row tiles of one column tile run together and share b's slab in L2.
   // 256-row tiles: the column tiles of one row tile run together and share a's rows in L2 (each
   // expert's weights are streamed once either way); measured 1.8x faster for them.
-  p.group_m = fp8g::tile_rows(cfg) == 256 ? 1 : p.tiles_m;
-  const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
+  p.group_m = fp8g::group_m_override(fp8g::tile_rows(cfg) == 256 ? 1 : p.tiles_m);
+  const int64_t grid = mul_sat(p.tiles_m, p.tiles_n);
   require(grid <= kInt32Max, "too many tiles");
   const fp8g::GemmMode mode = pt ? (swiglu ? fp8g::MODE_CONTIG_PT_SWIGLU : fp8g::MODE_CONTIG_PT)
                                  : (swiglu ? fp8g::MODE_CONTIG_SWIGLU : fp8g::MODE_CONTIG);
@@ -507,15 +522,15 @@ fp8g_status_t fp8_batch_gemm_masked(const void* a, const void* b, const float* a
     if (fp8g::tile_override() >= 0) cfg = (fp8g::TileConfig)fp8g::tile_override();
     p.tiles_m = (int32_t)ceil_div(max_m, fp8g::tile_rows(cfg));
     p.tiles_n = (int32_t)ceil_div(n, fp8g::tile_cols(cfg));
-    p.group_m = p.tiles_m;
-    const int64_t grid = (int64_t)num_groups * p.tiles_m * p.tiles_n;
+    p.group_m = fp8g::group_m_override(p.tiles_m);
+    const int64_t grid = mul_sat(num_groups, mul_sat(p.tiles_m, p.tiles_n));
     require(grid <= kInt32Max, "too many tiles");
     launch_logged("fp8_batch_gemm_masked launch", fp8g::MODE_MASKED, cfg, p, grid, stream);
   });
 }
 
 int64_t fp8_moe_permutation_workspace_size(int64_t num_tokens, int64_t top_k, int64_t num_experts) {
-  if (num_tokens < 0 || top_k < 0 || num_experts < 1 || num_experts > 1024 || num_tokens * top_k > kInt32Max)
+  if (num_tokens < 0 || top_k < 0 || num_experts < 1 || num_experts > 1024 || mul_sat(num_tokens, top_k) > kInt32Max)
     return -1;
   return 4 * fp8g::moe_permutation_scratch_ints(num_tokens * top_k, num_experts);
 }
@@ -530,7 +545,7 @@ bool check_permutation(const int32_t* topk_ids, int64_t num_tokens, int64_t top_
                        const int32_t* row_of_entry) {
   require(num_tokens >= 0 && top_k >= 0 && num_experts >= 1 && m_alloc >= 0, "sizes must be non-negative, num_experts >= 1");
   require(num_experts <= 1024, "num_experts must be at most 1024");
-  require(num_tokens * top_k <= kInt32Max && m_alloc <= kInt32Max, "sizes must fit in int32");
+  require(mul_sat(num_tokens, top_k) <= kInt32Max && m_alloc <= kInt32Max, "sizes must fit in int32");
   require(m_alloc % 128 == 0, "m_alloc must be a multiple of 128");
   const int64_t need = ceil_div(num_tokens * top_k + num_experts * 127, 128) * 128;
   require(m_alloc >= need, "m_alloc (%lld) must be at least %lld for this many entries and experts",
@@ -629,7 +644,8 @@ fp8g_status_t fp8_bmm(const void* a, const void* b, const float* a_scale, int32_
     require(a_scale_per_row == 0 || a_scale_per_row == 1, "a_scale_per_row must be 0 or 1");
     require(b_scale_per_col == 0 || b_scale_per_col == 1, "b_scale_per_col must be 0 or 1");
     if (batch == 0 || m == 0 || n == 0) return;
-    require(batch * m * n <= ((int64_t)1 << 40) && batch * n * k <= ((int64_t)1 << 40), "sizes too large");
+    require(mul_sat(batch, mul_sat(m, n)) <= ((int64_t)1 << 40) && mul_sat(batch, mul_sat(n, k)) <= ((int64_t)1 << 40),
+            "sizes too large");
     require(out && a_scale && b_scale, "out and the scales must be non-null");
     require(k == 0 || (a && b && workspace), "a, b and the workspace must be non-null");
     require(workspace_bytes >= batch * n * k, "workspace (%lld bytes) must hold batch*n*k = %lld bytes",
@@ -666,7 +682,7 @@ fp8g_status_t fp8_bmm(const void* a, const void* b, const float* a_scale, int32_
     p.tiles_m = (int32_t)ceil_div(m, fp8g::tile_rows(cfg));
     p.tiles_n = (int32_t)ceil_div(n, fp8g::tile_cols(cfg));
     p.group_m = 4;
-    const int64_t grid = batch * p.tiles_m * p.tiles_n;
+    const int64_t grid = mul_sat(batch, mul_sat(p.tiles_m, p.tiles_n));
     require(grid <= kInt32Max, "too many tiles");
     launch_logged("fp8_bmm launch", fp8g::MODE_BMM, cfg, p, grid, stream);
   });

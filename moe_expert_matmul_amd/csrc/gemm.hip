@@ -54,6 +54,9 @@ namespace kernels {
 constexpr int LOAD_GROUPS = 4;
 constexpr int LOAD_GROUPS_DEFER = 6;
 constexpr int BPRE = 1;  // measured against 2 and 3: the expert FFN 1.5% faster, the plain form level
+#ifndef FP8G_POISON_LDS
+#define FP8G_POISON_LDS 0
+#endif
 #ifndef FP8G_LDS_EPILOGUE
 #define FP8G_LDS_EPILOGUE 1
 #endif
@@ -240,6 +243,13 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in an SGPR
+#if FP8G_POISON_LDS
+  // Debug build: LDS starts as 0x7F bytes (E4M3 NaN codes; 3.4e38 as an FP32 scale), so a fragment or
+  // scale read that ran ahead of its load would reach the output.
+  for (int i = threadIdx.x * 16; i < (int)sizeof(smem); i += T::NTHREADS * 16)
+    *reinterpret_cast<uint4*>(smem + i) = uint4{0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
+  __syncthreads();
+#endif
 
   // ---- tile scheduling ---------------------------------------------------------------------
   int t = xcd_local_order(blockIdx.x, gridDim.x);

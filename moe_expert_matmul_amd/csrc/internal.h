@@ -69,6 +69,9 @@ enum TileConfig : int {
 // average); with 256-row tiles the grid holds one entry per 128-row half, and a tile whose halves
 // belong to different experts runs as two workgroups, each covering its own half.
 int tile_override();
+// Row tiles per raster group, forced through the FP8G_GROUP_M environment variable (a positive
+// integer), read at every call; `group_m` when unset. Tile order only: results never change.
+int group_m_override(int group_m);
 
 int tile_rows(TileConfig cfg);
 int tile_cols(TileConfig cfg);

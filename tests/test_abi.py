@@ -201,3 +201,24 @@ def test_header_and_library_work_from_plain_c(tmp_path):
     assert build.returncode == 0, build.stderr
     run = subprocess.run([str(exe)], capture_output=True, text=True)
     assert run.returncode == 0 and run.stdout.strip() == "ok", (run.returncode, run.stdout, run.stderr)
+
+
+def test_validation_layer_under_host_asan_and_ubsan(tmp_path):
+    """The library rebuilt with AddressSanitizer and UndefinedBehaviorSanitizer on its host code, driven
+    through every entry point's validation and error paths from C (no GPU is touched); any sanitizer
+    report fails the run."""
+    from moe_expert_matmul_amd import build as _build
+    lib_dir = tmp_path / "hostsan"
+    _build.build_host_sanitized(str(lib_dir))
+    clang = os.path.join(os.path.dirname(os.path.realpath(_build._hipcc())), "..", "lib", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/lib/llvm/bin/clang"
+    exe = tmp_path / "validation_under_sanitizers"
+    build = subprocess.run([clang, "-std=c99", "-Wall", "-Werror", "-g", "-fsanitize=address,undefined",
+                            "-fno-sanitize-recover=all", "-I", os.path.join(ROOT, "include"),
+                            os.path.join(ROOT, "tests", "c", "validation_under_sanitizers.c"), "-L", str(lib_dir),
+                            "-lfp8g", f"-Wl,-rpath,{lib_dir}", "-o", str(exe)], capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")
+    run = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=120)
+    assert run.returncode == 0 and run.stdout.startswith("ok"), (run.returncode, run.stdout, run.stderr[-3000:])
