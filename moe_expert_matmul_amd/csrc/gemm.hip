@@ -54,6 +54,9 @@ namespace kernels {
 constexpr int LOAD_GROUPS = 4;
 constexpr int LOAD_GROUPS_DEFER = 6;
 constexpr int BPRE = 1;  // measured against 2 and 3: the expert FFN 1.5% faster, the plain form level
+// a's row scales are fetched a group of K blocks at a time (Tile::SGRP), one group ahead, into a
+// ring of SA_SLOTS slots (see the load assignment in the kernel).
+constexpr int SA_SLOTS = 3;
 #ifndef FP8G_POISON_LDS
 #define FP8G_POISON_LDS 0
 #endif
@@ -72,9 +75,15 @@ struct Tile {
   static constexpr int JG = WTN / 16;
   static constexpr int A_BYTES = BM * KBLK;
   static constexpr int B_BYTES = BN * KBLK;
-  static constexpr int SA_OFF = A_BYTES + B_BYTES;  // BM floats: a's scales of the K block
-  static constexpr int SB_OFF = SA_OFF + BM * 4;    // 64 floats: b's scales (BN/128 used)
+  static constexpr int SB_OFF = A_BYTES + B_BYTES;  // 64 floats: b's scales (BN/128 used)
   static constexpr int STAGE_BYTES = SB_OFF + 64 * 4;
+  // a's row scales: a ring of SA_SLOTS slots after the stages, each the scales of SGRP K blocks
+  // for the BM rows (row r's SGRP values contiguous at byte 4 SGRP r). 8 blocks where the ring
+  // fits in LDS, else 4.
+  static constexpr int SA_RING_OFF = STAGES * STAGE_BYTES;
+  static constexpr int SGRP = SA_RING_OFF + SA_SLOTS * BM * 32 <= 160 * 1024 ? 8 : 4;
+  static constexpr int SA_SLOT = BM * SGRP * 4;
+  static constexpr int SMEM_BYTES = SA_RING_OFF + SA_SLOTS * SA_SLOT;
   static constexpr int A_LOADS = BM / SLAB_ROWS / NWAVES;  // per wave and K block
   static constexpr int B_LOADS = BN / SLAB_ROWS / NWAVES;
   static constexpr int LOADS = A_LOADS + B_LOADS + 1;      // + one scale load per wave
@@ -85,7 +94,8 @@ struct Tile {
   static_assert(128 % WTN == 0 || WTN == 128, "a wave's columns sit in one 128-wide b-scale block (two with SWIGLU)");
   static_assert(STAGES >= 2 && STAGES <= 4, "two to four LDS stages");
   static_assert((STAGES - 2) * LOADS < 64, "vmcnt range");
-  static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
+  static_assert(SMEM_BYTES <= 160 * 1024, "LDS");
+  static_assert(64 % SGRP == 0, "a group's part covers 64 / SGRP rows");
 };
 
 __device__ __forceinline__ float bf16_round(float x) { return (float)(__bf16)x; }  // RNE
@@ -239,7 +249,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   // first of the loads issued during column group jg (the LOADS loads spread over JG groups)
   constexpr int LG = T::JG < LOAD_GROUPS ? T::JG : LOAD_GROUPS;
   constexpr auto load_first = [](int jg) { return ((jg < LG ? jg : LG) * T::LOADS + LG - 1) / LG; };
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * T::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::SMEM_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in an SGPR
@@ -369,12 +379,37 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
       a_src[q] = (gathered[q] >= 0 && gathered[q] < p.a_src_rows) ? gathered[q] : 0;
   }
   uint32_t a_off[T::A_LOADS], b_off[T::B_LOADS];
+  // Bit q: a slab q of this wave holds a row whose output the tile keeps. A slab with no such row
+  // (rows past the group's valid count, padding rows, rows of the other expert in a split tile)
+  // is read out of range: no memory traffic (clamped or gathered rows would otherwise re-read one
+  // row many times over), zeros in LDS, rows never stored.
+  uint32_t a_live_bits = 0;
 #pragma unroll
   for (int q = 0; q < T::A_LOADS; ++q) {
     const int slab_row = (wave * T::A_LOADS + q) * SLAB_ROWS;
     const int lchunk = (lane & 7) ^ swizzle(slab_row + lrow);
     a_off[q] = (uint32_t)a_src[q] * (uint32_t)p.k + lchunk * 16;
+    bool live;
+    if constexpr (CONTIG) {
+      // m_indices entry of the slab row this lane loads: lane (row % 64) of the row's quarter
+      const int quarter = slab_row >> 6;
+      int ids = tile_ids[0];
+#pragma unroll
+      for (int r = 1; r < QUARTERS; ++r)
+        if (quarter == r) ids = tile_ids[r];
+      const int id = __shfl(ids, (slab_row & 63) + lrow, 64);
+      live = __ballot(id == bsel && ((half_mask >> (slab_row / 128)) & 1)) != 0;
+    } else {
+      live = row0 + slab_row < row_end;
+    }
+    a_live_bits |= (uint32_t)live << q;
   }
+  a_live_bits = __builtin_amdgcn_readfirstlane(a_live_bits);
+  // A dead slab's offset lies past the operand: out of the resource's range the load touches no
+  // memory and writes zeros (or, for an operand of 2 GiB or more, reads bytes of a inside its range).
+#pragma unroll
+  for (int q = 0; q < T::A_LOADS; ++q)
+    if (!((a_live_bits >> q) & 1)) a_off[q] = 0x80000000u;
 #pragma unroll
   for (int q = 0; q < T::B_LOADS; ++q) {
     const int slab_row = (wave * T::B_LOADS + q) * SLAB_ROWS;
@@ -390,23 +425,49 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(A, (uint32_t)p.a_src_rows * (uint32_t)p.k);
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(B, (uint32_t)p.n * (uint32_t)p.k);
 
-  // Scales of a K block travel with its slabs: waves 0 .. BM/64-1 each fetch 64 of a's row
-  // scales, every other wave fetches b's BN/128 block scales (identical data to the same place).
+  // Scales. Every wave issues one 4-byte-per-lane scale load per K block. Waves BM/64 and up fetch
+  // b's BN/128 block scales of the block (identical data to the same place) into its stage. Waves
+  // 0 .. BM/64-1 own 64 rows each and fetch a's row scales a group of G = SGRP K blocks at a time,
+  // in G parts: the load issued with block kb's slabs fetches part kb % G of group kb / G + 1, so a
+  // group is complete one group before its first block; group 0 is fetched ahead of the pipeline.
+  // A part is the shape that touches the fewest lines: in the K-major layout 64/G rows x G blocks
+  // (lane l: row l / G, block l % G; a row's G blocks are 4G contiguous bytes), so an instruction
+  // touches 64/G lines where a per-block fetch would touch 64; in the MN-major layout, and for
+  // gathered rows, one block of all 64 rows (lane l: row l). In LDS, the scale of row r (of the
+  // wave's 64) and block b of the group sits at byte 4G r + 4b (row parts) or 4r + 256b (block
+  // parts) of the wave's 256G bytes. Group g sits in slot g % 3: it is written while blocks of
+  // groups g-1 and g-2 may still be read, never g-3's. Part qq's offset is part 0's plus qq times a
+  // scalar step (0 for the b-scale waves: selecting between vector values on a wave-uniform
+  // condition would make the compiler split the scheduled loop body). Rows past the end read zeros
+  // or unused scales, both within the buffer; such rows are never stored.
+  constexpr int SGRP = T::SGRP;
+  constexpr int PART_ROWS = 64 / SGRP;
   const bool a_scale_wave = wave < BM / 64;
-  uint32_t s_voff;
-  int s_dst;
+  const bool sa_block_parts = p.sa_kb_stride != 1 || (CONTIG && p.a_rows != nullptr);
+  const int sa_lds_row = sa_block_parts ? 4 : 4 * SGRP;  // LDS bytes per row and per block
+  const int sa_lds_blk = sa_block_parts ? 256 : 4;
+  uint32_t s_voff0;
+  const uint32_t s_qstep = !a_scale_wave ? 0u
+                           : sa_block_parts ? (uint32_t)p.sa_kb_stride * 4u
+                                            : (uint32_t)PART_ROWS * (uint32_t)p.sa_row_stride * 4u;
   if (a_scale_wave) {
-    s_voff = (uint32_t)a_src[T::A_LOADS] * p.sa_row_stride * 4;
-    s_dst = T::SA_OFF + wave * 256;
+    // gathered rows: the lane's own row's source row, loaded with the m_indices
+    const int src_row = CONTIG && p.a_rows != nullptr ? a_src[T::A_LOADS]
+                                                      : row0 + wave * 64 + (sa_block_parts ? lane : lane / SGRP);
+    const uint32_t blk_off = sa_block_parts ? 0u : (uint32_t)(lane % SGRP) * p.sa_kb_stride * 4;
+    s_voff0 = (uint32_t)src_row * p.sa_row_stride * 4 + blk_off;
   } else {
     const int nb = SWIGLU ? min((lane == 0 ? 0 : p.inter / 128) + tn, p.nblocks - 1)
                           : min(col0 / 128 + lane, p.nblocks - 1);
-    s_voff = (uint32_t)nb * p.sb_nb_stride * 4;
-    s_dst = T::SB_OFF;
+    s_voff0 = (uint32_t)nb * p.sb_nb_stride * 4;
   }
   const uint32_t s_kb_bytes = (uint32_t)(a_scale_wave ? p.sa_kb_stride : p.sb_kb_stride) * 4;
-  const __amdgpu_buffer_rsrc_t rS = a_scale_wave ? make_rsrc(SA, (uint32_t)p.a_src_rows * p.kblocks * 4)
-                                                 : make_rsrc(SB, (uint32_t)p.nblocks * p.kblocks * 4);
+  // (built from values made explicitly wave-uniform: the compiler otherwise keeps the descriptor in
+  // vector registers and wraps every scale load in a loop over its distinct values)
+  const __amdgpu_buffer_rsrc_t rS =
+      make_rsrc(uniform_ptr(a_scale_wave ? (const void*)SA : (const void*)SB),
+                __builtin_amdgcn_readfirstlane(a_scale_wave ? (uint32_t)p.a_src_rows * p.kblocks * 4
+                                                            : (uint32_t)p.nblocks * p.kblocks * 4));
 
   // ---- this wave's output block --------------------------------------------------------------
   // Waves are numbered row-major over the WM x WN wave grid. Waves are dealt to the CU's 4 SIMDs
@@ -432,32 +493,60 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
 
   f32x4 acc[T::IG][T::JG];
 
-  // Load i of the LOADS per wave and K block: a slabs, then b slabs, then the scales.
-  // A zero-size resource: loads through it touch no memory and write zeros into LDS. The
-  // pipeline uses it for the blocks past the end of K, so every iteration issues the same loads.
+  // A zero-size resource: loads through it touch no memory and write zeros into LDS. The pipeline
+  // uses it for the blocks past the end of K, so that every iteration issues the same loads (and
+  // the scale loads of the modes that apply the scales in the epilogue).
   const __amdgpu_buffer_rsrc_t rNone = make_rsrc(A, 0);
+  const __amdgpu_buffer_rsrc_t rSc = NO_PROMOTION ? rNone : rS;
 
-  // Load i of the LOADS per wave for K block kb (a slabs, then b slabs, then the scales) into
-  // stage kb % STAGES; `live` false sends it through rNone.
-  auto issue_load = [&](int kb, int i, bool live) {
+  // Load i of the LOADS per wave for K block kb (the scales, then a slabs, then b slabs) into
+  // stage kb % STAGES, through the resources of the current iteration: rNone for the blocks past
+  // the end of K. They are picked once per iteration (set_load_rsrc), not per load, and by
+  // selects, not branches: a branch would split the scheduled block. The scale load goes first:
+  // its lines are scattered (a's rows), and issued behind the slabs it finished last (measured:
+  // the contiguous form 8% faster, the expert FFN 5%).
+  __amdgpu_buffer_rsrc_t rA_it = rA, rB_it = rB, rS_it = rSc;
+  auto set_load_rsrc = [&](bool live) {
+    rA_it = live ? rA : rNone;
+    rB_it = live ? rB : rNone;
+    rS_it = live ? rSc : rNone;
+  };
+  auto issue_load = [&](int kb, int i) {
     uint8_t* sA = smem + (kb % STAGES) * T::STAGE_BYTES;
     const uint32_t koff = (uint32_t)kb * KBLK;
-    if (i < T::A_LOADS) {
-      // slabs of a 128-row half this workgroup does not cover are not fetched
-      const int half_live = __builtin_amdgcn_readfirstlane((half_mask >> ((wave * T::A_LOADS + i) * SLAB_ROWS / 128)) & 1);
-      load_lds_16(live && half_live ? rA : rNone, sA + (wave * T::A_LOADS + i) * 1024, a_off[i], koff);
-    } else if (i < T::A_LOADS + T::B_LOADS) {
-      const int q = i - T::A_LOADS;
-      load_lds_16(live ? rB : rNone, sA + T::A_BYTES + (wave * T::B_LOADS + q) * 1024, b_off[q], koff);
+    if (i == 0) {
+      const int qq = kb & (SGRP - 1), grp = kb / SGRP + 1;
+      uint8_t* dst = a_scale_wave ? smem + T::SA_RING_OFF + (grp % SA_SLOTS) * T::SA_SLOT + wave * 256 * SGRP + qq * 256
+                                  : sA + T::SB_OFF;
+      const uint32_t soff = (uint32_t)(a_scale_wave ? grp * SGRP : kb) * s_kb_bytes;
+      load_lds_4(rS_it, dst, s_voff0 + (uint32_t)qq * s_qstep, soff);
+    } else if (i <= T::A_LOADS) {
+      const int q = i - 1;
+      load_lds_16(rA_it, sA + (wave * T::A_LOADS + q) * 1024, a_off[q], koff);
     } else {
-      // BMM: the scales act in the epilogue; the load still runs (through rNone) so that every
-      // mode issues the same loads per K block
-      load_lds_4(live && !NO_PROMOTION ? rS : rNone, sA + s_dst, s_voff, (uint32_t)kb * s_kb_bytes);
+      const int q = i - 1 - T::A_LOADS;
+      load_lds_16(rB_it, sA + T::A_BYTES + (wave * T::B_LOADS + q) * 1024, b_off[q], koff);
     }
   };
-  auto issue_loads = [&](int kb, bool live) {
+  // a's row scales of group 0 (K blocks 0 .. SGRP-1), ahead of the pipeline
+  auto issue_scale_group0 = [&]() {
+    if (a_scale_wave) {
 #pragma unroll
-    for (int i = 0; i < T::LOADS; ++i) issue_load(kb, i, live);
+      for (int qq = 0; qq < SGRP; ++qq)
+        load_lds_4(rSc, smem + T::SA_RING_OFF + wave * 256 * SGRP + qq * 256, s_voff0 + (uint32_t)qq * s_qstep, 0);
+    }
+  };
+  // a's scale of row i0 + 16 ig + fr (this lane's row of 16-row group ig) for K block kb. A wave's
+  // rows lie in one 64-row part of the ring (WTM == 64), so the lane's offset is fixed.
+  static_assert(T::WTM == 64, "a wave's rows are one a-scale wave's rows");
+  const int sa_lane_off = T::SA_RING_OFF + (i0 / 64) * 256 * SGRP + fr * sa_lds_row;
+  auto a_scale_at = [&](int kb, int ig) {
+    const int sc = ((kb / SGRP) % SA_SLOTS) * T::SA_SLOT + ig * 16 * sa_lds_row + (kb & (SGRP - 1)) * sa_lds_blk;
+    return *reinterpret_cast<const float*>(smem + sa_lane_off + sc);
+  };
+  auto issue_loads = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < T::LOADS; ++i) issue_load(kb, i);
   };
 
   // One K block of this wave's MFMAs and promotions, in explicit issue order. The body is cut into
@@ -468,7 +557,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   // read of its own result and no LDS read is hoisted far ahead of its use.
   // BMM: the same issue order without scales -- each MFMA accumulates straight into acc, over all
   // of K, and the scales are applied once in the epilogue.
-  auto compute_bmm = [&](int kb, int kb_load, bool load_live) {
+  auto compute_bmm = [&](int kb, int kb_load) {
     const uint8_t* sA = smem + (kb % STAGES) * T::STAGE_BYTES;
     const uint8_t* sB = sA + T::A_BYTES;
     i32x8 af[T::IG];
@@ -481,7 +570,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
 #pragma unroll
     for (int jg = 0; jg < T::JG; ++jg) {
 #pragma unroll
-      for (int i = load_first(jg); i < load_first(jg + 1); ++i) issue_load(kb_load, i, load_live);
+      for (int i = load_first(jg); i < load_first(jg + 1); ++i) issue_load(kb_load, i);
       if (jg + BPRE < T::JG) bq[jg + BPRE] = load_frag(sB, j0 + (jg + BPRE) * 16 + fr, lane);
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -496,17 +585,16 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     }
   };
 
-  auto compute = [&](int kb, int kb_load, bool load_live) {
+  auto compute = [&](int kb, int kb_load) {
     const uint8_t* sA = smem + (kb % STAGES) * T::STAGE_BYTES;
     const uint8_t* sB = sA + T::A_BYTES;
-    const float* sSA = reinterpret_cast<const float*>(sA + T::SA_OFF);
     const float* sSB = reinterpret_cast<const float*>(sA + T::SB_OFF);
     const float sbv = SWIGLU ? sSB[0] : sSB[(col0 + j0) / 128 - col0 / 128];
     const float sbv_up = SWIGLU ? sSB[1] : sbv;  // SWIGLU: the up columns' block
     float s[T::IG], s_up[T::IG];
 #pragma unroll
     for (int ig = 0; ig < T::IG; ++ig) {
-      const float sav = sSA[i0 + ig * 16 + fr];
+      const float sav = a_scale_at(kb, ig);
       s[ig] = sav * sbv;
       s_up[ig] = SWIGLU ? sav * sbv_up : s[ig];
     }
@@ -521,7 +609,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
 #pragma unroll
     for (int jg = 0; jg < T::JG; ++jg) {
 #pragma unroll
-      for (int i = load_first(jg); i < load_first(jg + 1); ++i) issue_load(kb_load, i, load_live);
+      for (int i = load_first(jg); i < load_first(jg + 1); ++i) issue_load(kb_load, i);
       if (jg + BPRE < T::JG) bq[jg + BPRE] = load_frag(sB, j0 + (jg + BPRE) * 16 + fr, lane);
       __builtin_amdgcn_s_setprio(1);  // favour the wave that is issuing MFMAs
 #pragma unroll
@@ -567,16 +655,15 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   float dq_s[T::IG];   // sa*sb of the block being computed
   float dq_sp[T::IG];  // sa*sb of the previous block, for its deferred promotions
 
-  auto compute_deferred = [&](int kb, int kb_load, bool load_live, bool first) {
+  auto compute_deferred = [&](int kb, int kb_load, bool first) {
     const uint8_t* sA = smem + (kb % STAGES) * T::STAGE_BYTES;
     const uint8_t* sB = sA + T::A_BYTES;
-    const float* sSA = reinterpret_cast<const float*>(sA + T::SA_OFF);
     const float* sSB = reinterpret_cast<const float*>(sA + T::SB_OFF);
 #pragma unroll
     for (int ig = 0; ig < T::IG; ++ig) dq_sp[ig] = dq_s[ig];
     const float sbv = sSB[(col0 + j0) / 128 - col0 / 128];
 #pragma unroll
-    for (int ig = 0; ig < T::IG; ++ig) dq_s[ig] = sSA[i0 + ig * 16 + fr] * sbv;
+    for (int ig = 0; ig < T::IG; ++ig) dq_s[ig] = a_scale_at(kb, ig) * sbv;
     dq_b[0] = load_frag(sB, j0 + fr, lane);
     __builtin_amdgcn_sched_barrier(0);
     if (!first) {
@@ -610,7 +697,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
 #pragma unroll
     for (int jg = 0; jg < T::JG - 1; ++jg) {
 #pragma unroll
-      for (int i = load_first_d(jg); i < load_first_d(jg + 1); ++i) issue_load(kb_load, i, load_live);
+      for (int i = load_first_d(jg); i < load_first_d(jg + 1); ++i) issue_load(kb_load, i);
       if (jg + BPRE < T::JG) dq_b[jg + BPRE] = load_frag(sB, j0 + (jg + BPRE) * 16 + fr, lane);
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -669,7 +756,13 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   for (int ig = 0; ig < T::IG; ++ig) dq_s[ig] = 0.0f;
   if (KB > 0) {
 #pragma unroll
-    for (int b = 0; b < STAGES - 1; ++b) issue_loads(b, b < KB);
+    for (int b = 0; b < STAGES - 1; ++b) {
+      set_load_rsrc(b < KB);
+      issue_loads(b);
+      // group 0 of a's scales after block 0's slabs (which it must not delay) and before block 1's
+      // (so that block 0's wait covers it)
+      if (b == 0) issue_scale_group0();
+    }
   }
 
   for (int kb = 0; kb < KB; ++kb) {
@@ -677,18 +770,19 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     wait_vmcnt<(STAGES - 2) * T::LOADS>();
     lds_pipeline_barrier();
     const int kb_load = kb + STAGES - 1;
+    set_load_rsrc(kb_load < KB);
     if (wave_live) {
       if constexpr (NO_PROMOTION)
-        compute_bmm(kb, kb_load, kb_load < KB);
+        compute_bmm(kb, kb_load);
       else if constexpr (DEFER) {
         if (kb == 0)
-          compute_deferred(kb, kb_load, kb_load < KB, true);
+          compute_deferred(kb, kb_load, true);
         else
-          compute_deferred(kb, kb_load, kb_load < KB, false);
+          compute_deferred(kb, kb_load, false);
       } else
-        compute(kb, kb_load, kb_load < KB);
+        compute(kb, kb_load);
     } else
-      issue_loads(kb_load, kb_load < KB);
+      issue_loads(kb_load);
   }
   if constexpr (DEFER) {
     if (wave_live && KB > 0) compute_deferred_tail();

@@ -68,6 +68,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// A pointer that is the same in every lane, moved into scalar registers.
+__device__ __forceinline__ const void* uniform_ptr(const void* ptr) {
+  const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
+}
+
 // 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 ... lds): lane l reads
 // byte offset voff + soff and writes bytes [16l, 16l+16) of the 1 KB block at the wave-uniform
 // address `lds`. soff is a scalar, so the per-lane offset is the only vector register used.
