@@ -110,26 +110,35 @@ def gemm_clock_mhz():
 
 
 def time_launches(fn, steps: int, warmup: int, probe: bool = False):
-    """W untimed launches, then `steps` back-to-back launches with an event before each and after the
-    last, on the launching stream. Returns (mean, median, min) ms per launch, the wall time of the
-    timed region, and the shader clock read right after it (when `probe`)."""
+    """W untimed launches, then `steps` back-to-back launches between two events on the launching
+    stream (the timed region: nothing else enters the stream between the launches), then `steps` more
+    with an event before each, for the spread. Returns (mean ms per launch over the timed region,
+    median and min ms per launch of the second pass), the wall time of the timed region, and the
+    shader clock read right after it (when `probe`)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    read_clock = sclk_probe() if probe else None
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mean = start.elapsed_time(end) / steps
+    clock = read_clock() if read_clock else None
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     for i in range(steps):
         ev[i].record(stream)
         fn()
     ev[steps].record(stream)
-    read_clock = sclk_probe() if probe else None
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
-    mean = ev[0].elapsed_time(ev[steps]) / steps
-    return mean, per[len(per) // 2], per[0], wall, (read_clock() if read_clock else None)
+    return mean, per[len(per) // 2], per[0], wall, clock
 
 
 def time_cold(fn, steps: int, warmup: int, flush):
