@@ -430,32 +430,42 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   // 0 .. BM/64-1 own 64 rows each and fetch a's row scales a group of G = SGRP K blocks at a time,
   // in G parts: the load issued with block kb's slabs fetches part kb % G of group kb / G + 1, so a
   // group is complete one group before its first block; group 0 is fetched ahead of the pipeline.
-  // A part is the shape that touches the fewest lines: in the K-major layout 64/G rows x G blocks
-  // (lane l: row l / G, block l % G; a row's G blocks are 4G contiguous bytes), so an instruction
-  // touches 64/G lines where a per-block fetch would touch 64; in the MN-major layout, and for
-  // gathered rows, one block of all 64 rows (lane l: row l). In LDS, the scale of row r (of the
-  // wave's 64) and block b of the group sits at byte 4G r + 4b (row parts) or 4r + 256b (block
-  // parts) of the wave's 256G bytes. Group g sits in slot g % 3: it is written while blocks of
-  // groups g-1 and g-2 may still be read, never g-3's. Part qq's offset is part 0's plus qq times a
-  // scalar step (0 for the b-scale waves: selecting between vector values on a wave-uniform
-  // condition would make the compiler split the scheduled loop body). Rows past the end read zeros
-  // or unused scales, both within the buffer; such rows are never stored.
+  // A part is the shape that touches the fewest lines: in the K-major layout PR = 64/G rows x G
+  // blocks (a row's G blocks are 4G contiguous bytes), so an instruction touches PR lines where a
+  // per-block fetch would touch 64; in the MN-major layout, and for gathered rows, one block of all
+  // 64 rows. In LDS each part is 256 bytes, block-major with the rows of a block in consecutive
+  // words, so the 16 consecutive rows a fragment's lanes read sit in 16 consecutive or (PR = 8)
+  // two 8-word runs; with PR = 8 the blocks of odd parts are stored XOR 2 (block b at position
+  // b ^ 2), which puts the two runs 64 bytes apart in the bank space instead of on the same banks.
+  // So the scale of row r (of the wave's 64) and block b sits at byte
+  //   row parts:   256 (r / PR) + 4 (PR (b ^ x) + r % PR), x = 2 ((r / PR) & 1) if PR = 8 else 0
+  //   block parts: 256 b + 4 r
+  // of the wave's 256G bytes, and lane l of part qq fetches row PR qq + l % PR, block (l / PR) ^ x.
+  // Group g sits in slot g % 3: it is written while blocks of groups g-1 and g-2 may still be read,
+  // never g-3's. Part qq's offset is part 0's plus qq times a scalar step, plus a per-lane term for
+  // odd qq (the swizzle; 0 for the b-scale waves, which have a zero step too: selecting between
+  // vector values on a wave-uniform condition would make the compiler split the scheduled loop
+  // body). Rows past the end read zeros or unused scales, both within the buffer; such rows are
+  // never stored.
   constexpr int SGRP = T::SGRP;
   constexpr int PART_ROWS = 64 / SGRP;
+  constexpr bool PART_SWIZZLE = PART_ROWS == 8;
   const bool a_scale_wave = wave < BM / 64;
   const bool sa_block_parts = p.sa_kb_stride != 1 || (CONTIG && p.a_rows != nullptr);
-  const int sa_lds_row = sa_block_parts ? 4 : 4 * SGRP;  // LDS bytes per row and per block
-  const int sa_lds_blk = sa_block_parts ? 256 : 4;
   uint32_t s_voff0;
+  uint32_t s_qodd = 0;  // added for odd parts: the block swizzle of row parts
   const uint32_t s_qstep = !a_scale_wave ? 0u
                            : sa_block_parts ? (uint32_t)p.sa_kb_stride * 4u
                                             : (uint32_t)PART_ROWS * (uint32_t)p.sa_row_stride * 4u;
   if (a_scale_wave) {
     // gathered rows: the lane's own row's source row, loaded with the m_indices
     const int src_row = CONTIG && p.a_rows != nullptr ? a_src[T::A_LOADS]
-                                                      : row0 + wave * 64 + (sa_block_parts ? lane : lane / SGRP);
-    const uint32_t blk_off = sa_block_parts ? 0u : (uint32_t)(lane % SGRP) * p.sa_kb_stride * 4;
+                                                      : row0 + wave * 64 + (sa_block_parts ? lane : lane % PART_ROWS);
+    const int blk = lane / PART_ROWS;
+    const uint32_t blk_off = sa_block_parts ? 0u : (uint32_t)blk * p.sa_kb_stride * 4;
     s_voff0 = (uint32_t)src_row * p.sa_row_stride * 4 + blk_off;
+    if (PART_SWIZZLE && !sa_block_parts)  // block blk ^ 2: two blocks on, or two back
+      s_qodd = (blk & 2) ? 0u - 2u * (uint32_t)p.sa_kb_stride * 4u : 2u * (uint32_t)p.sa_kb_stride * 4u;
   } else {
     const int nb = SWIGLU ? min((lane == 0 ? 0 : p.inter / 128) + tn, p.nblocks - 1)
                           : min(col0 / 128 + lane, p.nblocks - 1);
@@ -511,7 +521,11 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     rB_it = live ? rB : rNone;
     rS_it = live ? rSc : rNone;
   };
-  auto issue_load = [&](int kb, int i) {
+  auto issue_load = [&](int kb, int i_) {
+    // the deferred schedule (plain and masked forms) keeps the scale load last: first, it makes the
+    // compiler shuffle registers in that loop
+    constexpr bool SCALE_LAST = !NO_PROMOTION && (MODE == MODE_PLAIN || MODE == MODE_MASKED);
+    const int i = SCALE_LAST ? (i_ + 1) % T::LOADS : i_;
     uint8_t* sA = smem + (kb % STAGES) * T::STAGE_BYTES;
     const uint32_t koff = (uint32_t)kb * KBLK;
     if (i == 0) {
@@ -519,7 +533,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
       uint8_t* dst = a_scale_wave ? smem + T::SA_RING_OFF + (grp % SA_SLOTS) * T::SA_SLOT + wave * 256 * SGRP + qq * 256
                                   : sA + T::SB_OFF;
       const uint32_t soff = (uint32_t)(a_scale_wave ? grp * SGRP : kb) * s_kb_bytes;
-      load_lds_4(rS_it, dst, s_voff0 + (uint32_t)qq * s_qstep, soff);
+      load_lds_4(rS_it, dst, s_voff0 + (uint32_t)qq * s_qstep + (uint32_t)(qq & 1) * s_qodd, soff);
     } else if (i <= T::A_LOADS) {
       const int q = i - 1;
       load_lds_16(rA_it, sA + (wave * T::A_LOADS + q) * 1024, a_off[q], koff);
@@ -533,16 +547,25 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     if (a_scale_wave) {
 #pragma unroll
       for (int qq = 0; qq < SGRP; ++qq)
-        load_lds_4(rSc, smem + T::SA_RING_OFF + wave * 256 * SGRP + qq * 256, s_voff0 + (uint32_t)qq * s_qstep, 0);
+        load_lds_4(rSc, smem + T::SA_RING_OFF + wave * 256 * SGRP + qq * 256,
+                   s_voff0 + (uint32_t)qq * s_qstep + (uint32_t)(qq & 1) * s_qodd, 0);
     }
   };
   // a's scale of row i0 + 16 ig + fr (this lane's row of 16-row group ig) for K block kb. A wave's
   // rows lie in one 64-row part of the ring (WTM == 64), so the lane's offset is fixed.
   static_assert(T::WTM == 64, "a wave's rows are one a-scale wave's rows");
-  const int sa_lane_off = T::SA_RING_OFF + (i0 / 64) * 256 * SGRP + fr * sa_lds_row;
+  // Row r = 16 ig + fr of the wave's 64: row parts put it in part (16 ig + fr) / PR, the odd parts
+  // (fr >= 8 when PR = 8) with the block swizzle (block b at b ^ 2: 8 words on for b & 2 == 0, else
+  // back); block parts at word r of block b.
+  const int sa_lane_off = T::SA_RING_OFF + (i0 / 64) * 256 * SGRP +
+                          (sa_block_parts ? fr * 4 : (fr / PART_ROWS) * 256 + (fr % PART_ROWS) * 4);
+  const int sa_ig_step = sa_block_parts ? 64 : 16 / PART_ROWS * 256;
+  const int sa_blk_step = sa_block_parts ? 256 : 4 * PART_ROWS;
+  const int sa_lane_sw = (PART_SWIZZLE && !sa_block_parts && fr >= 8) ? 2 * 4 * PART_ROWS : 0;
   auto a_scale_at = [&](int kb, int ig) {
-    const int sc = ((kb / SGRP) % SA_SLOTS) * T::SA_SLOT + ig * 16 * sa_lds_row + (kb & (SGRP - 1)) * sa_lds_blk;
-    return *reinterpret_cast<const float*>(smem + sa_lane_off + sc);
+    const int b = kb & (SGRP - 1);
+    const int sc = ((kb / SGRP) % SA_SLOTS) * T::SA_SLOT + ig * sa_ig_step + b * sa_blk_step;
+    return *reinterpret_cast<const float*>(smem + sa_lane_off + sa_lane_sw * (1 - (b & 2)) + sc);
   };
   auto issue_loads = [&](int kb) {
 #pragma unroll
