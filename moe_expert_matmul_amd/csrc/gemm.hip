@@ -64,8 +64,13 @@ constexpr int SA_SLOTS = 3;
 #define FP8G_LDS_EPILOGUE 1
 #endif
 constexpr bool LDS_EPILOGUE = FP8G_LDS_EPILOGUE;
+#ifndef FP8G_SPLIT_PIPELINE
+#define FP8G_SPLIT_PIPELINE 1
+#endif
 
-template <int BM, int BN, int WM, int WN, int STAGES>
+// SPLIT: the split pipeline (see the kernel): one a buffer and STAGES + 1 b slots instead of
+// STAGES stages of both.
+template <int BM, int BN, int WM, int WN, int STAGES, bool SPLIT = false>
 struct Tile {
   static constexpr int NWAVES = WM * WN;
   static constexpr int NTHREADS = NWAVES * 64;
@@ -77,23 +82,27 @@ struct Tile {
   static constexpr int B_BYTES = BN * KBLK;
   static constexpr int SB_OFF = A_BYTES + B_BYTES;  // 64 floats: b's scales (BN/128 used)
   static constexpr int STAGE_BYTES = SB_OFF + 64 * 4;
+  // split pipeline: the a buffer at 0, then B_STAGES slots of b's slabs and scales
+  static constexpr int B_STAGES = SPLIT ? STAGES + 1 : STAGES;
+  static constexpr int B_SLOT = B_BYTES + 64 * 4;
   // a's row scales: a ring of SA_SLOTS slots after the stages, each the scales of SGRP K blocks
-  // for the BM rows (row r's SGRP values contiguous at byte 4 SGRP r). 8 blocks where the ring
-  // fits in LDS, else 4.
-  static constexpr int SA_RING_OFF = STAGES * STAGE_BYTES;
+  // for the BM rows. 8 blocks where the ring fits in LDS, else 4.
+  static constexpr int SA_RING_OFF = SPLIT ? A_BYTES + B_STAGES * B_SLOT : STAGES * STAGE_BYTES;
   static constexpr int SGRP = SA_RING_OFF + SA_SLOTS * BM * 32 <= 160 * 1024 ? 8 : 4;
   static constexpr int SA_SLOT = BM * SGRP * 4;
   static constexpr int SMEM_BYTES = SA_RING_OFF + SA_SLOTS * SA_SLOT;
   static constexpr int A_LOADS = BM / SLAB_ROWS / NWAVES;  // per wave and K block
   static constexpr int B_LOADS = BN / SLAB_ROWS / NWAVES;
   static constexpr int LOADS = A_LOADS + B_LOADS + 1;      // + one scale load per wave
+  // the loads spread over a block's column groups: all of them, or (split) b's and the scales
+  static constexpr int SPREAD_LOADS = SPLIT ? B_LOADS + 1 : LOADS;
   static_assert(BM / 64 < NWAVES, "one wave per 64 a-scale rows, and one more for b's scales");
-  static_assert(STAGE_BYTES % 256 == 0, "stages keep the slabs' bank alignment");
+  static_assert(STAGE_BYTES % 256 == 0 && B_SLOT % 256 == 0 && A_BYTES % 256 == 0, "stages keep the slabs' bank alignment");
   static_assert(BM % (SLAB_ROWS * NWAVES) == 0 && BN % (SLAB_ROWS * NWAVES) == 0, "slabs");
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "16x16 MFMA blocks");
   static_assert(128 % WTN == 0 || WTN == 128, "a wave's columns sit in one 128-wide b-scale block (two with SWIGLU)");
   static_assert(STAGES >= 2 && STAGES <= 4, "two to four LDS stages");
-  static_assert((STAGES - 2) * LOADS < 64, "vmcnt range");
+  static_assert((STAGES - 2) * LOADS < 64 && SPREAD_LOADS < 64, "vmcnt range");
   static_assert(SMEM_BYTES <= 160 * 1024, "LDS");
   static_assert(64 % SGRP == 0, "a group's part covers 64 / SGRP rows");
 };
@@ -237,18 +246,27 @@ template <int BM, int BN, int WM, int WN, int STAGES, int MODE>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_fp8_groupwise_kernel(const GemmParams p) {
   const ClockStamp stamp;
-  using T = Tile<BM, BN, WM, WN, STAGES>;
   constexpr bool PT = MODE == MODE_CONTIG_PT || MODE == MODE_CONTIG_PT_SWIGLU;
   constexpr bool CONTIG = MODE == MODE_CONTIG || MODE == MODE_CONTIG_SWIGLU || PT;
   constexpr bool SWIGLU = MODE == MODE_CONTIG_SWIGLU || MODE == MODE_CONTIG_PT_SWIGLU;
   constexpr bool NO_PROMOTION = MODE == MODE_BMM || PT;  // scales constant along K: applied at the end
+  // Split pipeline (the masked form's two-stage tiles): one a buffer and three b slots. Iteration
+  // kb computes block kb; once every wave has read its a fragments of block kb (a second barrier,
+  // mid-block), the a slabs of block kb+1 are loaded into the a buffer, and the b slabs and scales
+  // of block kb+2 go into a free b slot over the block's column groups. The b slabs, which stream
+  // from HBM, thus have two blocks to arrive instead of one, and a's (mostly L2 hits) one; 96 KB
+  // are in flight per workgroup instead of 64. Measured: the masked form 5% faster; the plain form
+  // (compute-bound) 11% and the contiguous form's 256-row tiles (fc2) 1-3% slower, so they keep
+  // the two stages.
+  constexpr bool SPLIT = FP8G_SPLIT_PIPELINE && STAGES == 2 && MODE == MODE_MASKED;
+  using T = Tile<BM, BN, WM, WN, STAGES, SPLIT>;
   // SWIGLU: wave column q of the WN holds the gate and the up columns of OUTW output columns; its
   // b rows ("virtual columns" v of the tile) are OUTW gate rows then OUTW up rows.
   constexpr int OUTW = SWIGLU ? 128 / WN : 0;
   static_assert(!SWIGLU || (BN == 256 && T::WTN == 2 * (128 / WN)), "SWIGLU tiles are 256 wide");
-  // first of the loads issued during column group jg (the LOADS loads spread over JG groups)
+  // first of the loads issued during column group jg (the SPREAD_LOADS loads spread over JG groups)
   constexpr int LG = T::JG < LOAD_GROUPS ? T::JG : LOAD_GROUPS;
-  constexpr auto load_first = [](int jg) { return ((jg < LG ? jg : LG) * T::LOADS + LG - 1) / LG; };
+  constexpr auto load_first = [](int jg) { return ((jg < LG ? jg : LG) * T::SPREAD_LOADS + LG - 1) / LG; };
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::SMEM_BYTES];
 
   const int lane = threadIdx.x & 63;
@@ -509,37 +527,63 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   const __amdgpu_buffer_rsrc_t rNone = make_rsrc(A, 0);
   const __amdgpu_buffer_rsrc_t rSc = NO_PROMOTION ? rNone : rS;
 
-  // Load i of the LOADS per wave for K block kb (the scales, then a slabs, then b slabs) into
-  // stage kb % STAGES, through the resources of the current iteration: rNone for the blocks past
-  // the end of K. They are picked once per iteration (set_load_rsrc), not per load, and by
-  // selects, not branches: a branch would split the scheduled block. The scale load goes first:
-  // its lines are scattered (a's rows), and issued behind the slabs it finished last (measured:
-  // the contiguous form 8% faster, the expert FFN 5%).
-  __amdgpu_buffer_rsrc_t rA_it = rA, rB_it = rB, rS_it = rSc;
-  auto set_load_rsrc = [&](bool live) {
-    rA_it = live ? rA : rNone;
-    rB_it = live ? rB : rNone;
-    rS_it = live ? rSc : rNone;
+  // Stages of K block kb: a's slabs, b's slabs, b's scales (after b's slabs).
+  auto a_stage = [&](int kb) -> uint8_t* { return SPLIT ? smem : smem + (kb % STAGES) * T::STAGE_BYTES; };
+  auto b_stage = [&](int kb) -> uint8_t* {
+    return SPLIT ? smem + T::A_BYTES + (kb % T::B_STAGES) * T::B_SLOT : smem + (kb % STAGES) * T::STAGE_BYTES + T::A_BYTES;
   };
+
+  // The loads of a K block go through the resources of the current iteration: rNone for the
+  // blocks past the end of K. They are picked once per iteration (set_load_rsrc), not per load, and
+  // by selects, not branches: a branch would split the scheduled block.
+  __amdgpu_buffer_rsrc_t rA_it = rA, rB_it = rB, rS_it = rSc;
+  auto set_load_rsrc = [&](bool a_live, bool b_live) {
+    rA_it = a_live ? rA : rNone;
+    rB_it = b_live ? rB : rNone;
+    rS_it = b_live ? rSc : rNone;
+  };
+  auto issue_a = [&](int kb, int q) {
+    load_lds_16(rA_it, a_stage(kb) + (wave * T::A_LOADS + q) * 1024, a_off[q], (uint32_t)kb * KBLK);
+  };
+  auto issue_b = [&](int kb, int q) {
+    load_lds_16(rB_it, b_stage(kb) + (wave * T::B_LOADS + q) * 1024, b_off[q], (uint32_t)kb * KBLK);
+  };
+  auto issue_s = [&](int kb) {
+    const int qq = kb & (SGRP - 1), grp = kb / SGRP + 1;
+    uint8_t* dst = a_scale_wave ? smem + T::SA_RING_OFF + (grp % SA_SLOTS) * T::SA_SLOT + wave * 256 * SGRP + qq * 256
+                                : b_stage(kb) + T::B_BYTES;
+    const uint32_t soff = (uint32_t)(a_scale_wave ? grp * SGRP : kb) * s_kb_bytes;
+    load_lds_4(rS_it, dst, s_voff0 + (uint32_t)qq * s_qstep + (uint32_t)(qq & 1) * s_qodd, soff);
+  };
+  // Spread load i of K block kb, i < SPREAD_LOADS: the scale load, then a's slabs (not in the split
+  // pipeline, which loads them at once), then b's. The scale load goes first: its lines are
+  // scattered (a's rows), and issued behind the slabs it finished last (measured: the contiguous
+  // form 8% faster, the expert FFN 5%); the deferred schedule keeps it last, as first it makes the
+  // compiler shuffle registers in that loop.
   auto issue_load = [&](int kb, int i_) {
-    // the deferred schedule (plain and masked forms) keeps the scale load last: first, it makes the
-    // compiler shuffle registers in that loop
     constexpr bool SCALE_LAST = !NO_PROMOTION && (MODE == MODE_PLAIN || MODE == MODE_MASKED);
-    const int i = SCALE_LAST ? (i_ + 1) % T::LOADS : i_;
-    uint8_t* sA = smem + (kb % STAGES) * T::STAGE_BYTES;
-    const uint32_t koff = (uint32_t)kb * KBLK;
-    if (i == 0) {
-      const int qq = kb & (SGRP - 1), grp = kb / SGRP + 1;
-      uint8_t* dst = a_scale_wave ? smem + T::SA_RING_OFF + (grp % SA_SLOTS) * T::SA_SLOT + wave * 256 * SGRP + qq * 256
-                                  : sA + T::SB_OFF;
-      const uint32_t soff = (uint32_t)(a_scale_wave ? grp * SGRP : kb) * s_kb_bytes;
-      load_lds_4(rS_it, dst, s_voff0 + (uint32_t)qq * s_qstep + (uint32_t)(qq & 1) * s_qodd, soff);
-    } else if (i <= T::A_LOADS) {
-      const int q = i - 1;
-      load_lds_16(rA_it, sA + (wave * T::A_LOADS + q) * 1024, a_off[q], koff);
-    } else {
-      const int q = i - 1 - T::A_LOADS;
-      load_lds_16(rB_it, sA + T::A_BYTES + (wave * T::B_LOADS + q) * 1024, b_off[q], koff);
+    const int i = SCALE_LAST ? (i_ + 1) % T::SPREAD_LOADS : i_;
+    if (i == 0)
+      issue_s(kb);
+    else if (!SPLIT && i <= T::A_LOADS)
+      issue_a(kb, i - 1);
+    else
+      issue_b(kb, i - 1 - (SPLIT ? 0 : T::A_LOADS));
+  };
+  auto issue_a_all = [&](int kb) {
+#pragma unroll
+    for (int q = 0; q < T::A_LOADS; ++q) issue_a(kb, q);
+  };
+  // Split pipeline, mid-block: once every wave has read its a fragments of block kb (its LDS reads
+  // retired, then the barrier), load block kb+1's. The memory clobber keeps those reads above the
+  // barrier; the loads, side effects like the barrier, stay below it. (Unlike lds_pipeline_barrier,
+  // no clobber after the barrier: with one, the deferred schedule spills registers.)
+  auto split_refill_a = [&](int kb) {
+    if constexpr (SPLIT) {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      issue_a_all(kb + 1);
     }
   };
   // a's row scales of group 0 (K blocks 0 .. SGRP-1), ahead of the pipeline
@@ -569,7 +613,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   };
   auto issue_loads = [&](int kb) {
 #pragma unroll
-    for (int i = 0; i < T::LOADS; ++i) issue_load(kb, i);
+    for (int i = 0; i < T::SPREAD_LOADS; ++i) issue_load(kb, i);
   };
 
   // One K block of this wave's MFMAs and promotions, in explicit issue order. The body is cut into
@@ -581,8 +625,8 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   // BMM: the same issue order without scales -- each MFMA accumulates straight into acc, over all
   // of K, and the scales are applied once in the epilogue.
   auto compute_bmm = [&](int kb, int kb_load) {
-    const uint8_t* sA = smem + (kb % STAGES) * T::STAGE_BYTES;
-    const uint8_t* sB = sA + T::A_BYTES;
+    const uint8_t* sA = a_stage(kb);
+    const uint8_t* sB = b_stage(kb);
     i32x8 af[T::IG];
 #pragma unroll
     for (int ig = 0; ig < T::IG; ++ig) af[ig] = load_frag(sA, i0 + ig * 16 + fr, lane);
@@ -609,9 +653,9 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   };
 
   auto compute = [&](int kb, int kb_load) {
-    const uint8_t* sA = smem + (kb % STAGES) * T::STAGE_BYTES;
-    const uint8_t* sB = sA + T::A_BYTES;
-    const float* sSB = reinterpret_cast<const float*>(sA + T::SB_OFF);
+    const uint8_t* sA = a_stage(kb);
+    const uint8_t* sB = b_stage(kb);
+    const float* sSB = reinterpret_cast<const float*>(sB + T::B_BYTES);
     const float sbv = SWIGLU ? sSB[0] : sSB[(col0 + j0) / 128 - col0 / 128];
     const float sbv_up = SWIGLU ? sSB[1] : sbv;  // SWIGLU: the up columns' block
     float s[T::IG], s_up[T::IG];
@@ -628,6 +672,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
 #pragma unroll
     for (int jg = 0; jg < BPRE && jg < T::JG; ++jg) bq[jg] = load_frag(sB, j0 + jg * 16 + fr, lane);
     __builtin_amdgcn_sched_barrier(0);
+    split_refill_a(kb);
     f32x4 prod[T::JG][T::IG];
 #pragma unroll
     for (int jg = 0; jg < T::JG; ++jg) {
@@ -670,7 +715,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   // registers with it, so the grouped forms keep `compute`.)
   constexpr bool DEFER = !NO_PROMOTION && (MODE == MODE_PLAIN || MODE == MODE_MASKED);
   constexpr int LGD = (T::JG - 1) < LOAD_GROUPS_DEFER ? (T::JG - 1) : LOAD_GROUPS_DEFER;
-  constexpr auto load_first_d = [](int jg) { return ((jg < LGD ? jg : LGD) * T::LOADS + LGD - 1) / LGD; };
+  constexpr auto load_first_d = [](int jg) { return ((jg < LGD ? jg : LGD) * T::SPREAD_LOADS + LGD - 1) / LGD; };
   static_assert(!DEFER || (T::JG >= 3 && BPRE < T::JG), "the deferred schedule needs three column groups");
   i32x8 dq_a[T::IG];
   i32x8 dq_b[T::JG];
@@ -679,9 +724,9 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   float dq_sp[T::IG];  // sa*sb of the previous block, for its deferred promotions
 
   auto compute_deferred = [&](int kb, int kb_load, bool first) {
-    const uint8_t* sA = smem + (kb % STAGES) * T::STAGE_BYTES;
-    const uint8_t* sB = sA + T::A_BYTES;
-    const float* sSB = reinterpret_cast<const float*>(sA + T::SB_OFF);
+    const uint8_t* sA = a_stage(kb);
+    const uint8_t* sB = b_stage(kb);
+    const float* sSB = reinterpret_cast<const float*>(sB + T::B_BYTES);
 #pragma unroll
     for (int ig = 0; ig < T::IG; ++ig) dq_sp[ig] = dq_s[ig];
     const float sbv = sSB[(col0 + j0) / 128 - col0 / 128];
@@ -716,6 +761,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
 #pragma unroll
     for (int jg = 1; jg < BPRE; ++jg) dq_b[jg] = load_frag(sB, j0 + jg * 16 + fr, lane);
     __builtin_amdgcn_sched_barrier(0);
+    split_refill_a(kb);
     // groups 0 .. JG-2 of block kb; group 0's MFMAs carry the last promotions of block kb-1
 #pragma unroll
     for (int jg = 0; jg < T::JG - 1; ++jg) {
@@ -778,22 +824,36 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
 #pragma unroll
   for (int ig = 0; ig < T::IG; ++ig) dq_s[ig] = 0.0f;
   if (KB > 0) {
+    if constexpr (SPLIT) {
+      // a and b of block 0, a's scale group 0, b of block 1 (block 0's wait covers all but the last)
+      set_load_rsrc(true, true);
+      issue_a_all(0);
+      issue_loads(0);
+      issue_scale_group0();
+      set_load_rsrc(true, 1 < KB);
+      issue_loads(1);
+    } else {
 #pragma unroll
-    for (int b = 0; b < STAGES - 1; ++b) {
-      set_load_rsrc(b < KB);
-      issue_loads(b);
-      // group 0 of a's scales after block 0's slabs (which it must not delay) and before block 1's
-      // (so that block 0's wait covers it)
-      if (b == 0) issue_scale_group0();
+      for (int b = 0; b < STAGES - 1; ++b) {
+        set_load_rsrc(b < KB, b < KB);
+        issue_loads(b);
+        // group 0 of a's scales after block 0's slabs (which it must not delay) and before block
+        // 1's (so that block 0's wait covers it)
+        if (b == 0) issue_scale_group0();
+      }
     }
   }
 
   for (int kb = 0; kb < KB; ++kb) {
     // block kb has landed once at most the loads of blocks kb+1 .. kb+STAGES-2 are in flight
-    wait_vmcnt<(STAGES - 2) * T::LOADS>();
+    // (split: b's and the scales of block kb+1, issued after a's slabs of block kb)
+    if constexpr (SPLIT)
+      wait_vmcnt<T::SPREAD_LOADS>();
+    else
+      wait_vmcnt<(STAGES - 2) * T::LOADS>();
     lds_pipeline_barrier();
-    const int kb_load = kb + STAGES - 1;
-    set_load_rsrc(kb_load < KB);
+    const int kb_load = kb + (SPLIT ? 2 : STAGES - 1);
+    set_load_rsrc(kb + (SPLIT ? 1 : STAGES - 1) < KB, kb_load < KB);
     if (wave_live) {
       if constexpr (NO_PROMOTION)
         compute_bmm(kb, kb_load);
@@ -804,8 +864,10 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
           compute_deferred(kb, kb_load, false);
       } else
         compute(kb, kb_load);
-    } else
+    } else {
+      split_refill_a(kb);  // the same barriers as the computing waves
       issue_loads(kb_load);
+    }
   }
   if constexpr (DEFER) {
     if (wave_live && KB > 0) compute_deferred_tail();
@@ -832,7 +894,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   constexpr bool LDS_EPI_MODE = MODE == MODE_PLAIN || MODE == MODE_MASKED || MODE == MODE_CONTIG ||
                                 MODE == MODE_CONTIG_PT;
   if constexpr (LDS_EPILOGUE && LDS_EPI_MODE) {
-    static_assert(BM * BN * 2 + BM <= STAGES * T::STAGE_BYTES, "the output tile and its row flags fit in the stages");
+    static_assert(BM * BN * 2 + BM <= T::SA_RING_OFF, "the output tile and its row flags fit in the stages");
     if (p.out_scale == nullptr && (p.n & 7) == 0 && col0 + BN <= p.n) {  // uniform
       constexpr int PITCH = BN * 2;  // bytes per tile row
       uint8_t* row_flag = smem + BM * BN * 2;

@@ -331,17 +331,21 @@ def test_masked_matches_oracle_and_leaves_other_rows(expected_m):
         assert not keep[g, :mm[g]].any()
 
 
-@pytest.mark.parametrize("k", [128, 256])
+@pytest.mark.parametrize("k", [128, 256, 384, 1152])
 def test_masked_short_k_matches_oracle(k):
-    """One and two K blocks: the masked form's schedule carries each block's last column group
-    into the next block, so these cover a loop that is all first block and tail."""
+    """One to nine K blocks: the masked form's schedule carries each block's last column group
+    into the next block, and its 256-row tiles load b two blocks ahead into three slots and a's
+    row scales eight blocks at a time, so these cover loops that are all prologue and tail, every
+    slot phase, and a second scale group (k = 1152), in both scale layouts."""
     G, max_m, n = 3, 256, 384
     mm = np.array([256, 70, 129], np.int32)
     say("masked short k", G, max_m, n, k, mm.tolist())
     for expected_m in (32, 256):  # 128- and 256-row tiles
         d = workloads.masked(G, max_m, n, k, expected_m, seed=11 + k, device=DEV, masked_m=mm)
-        out = _masked_call(d)
-        assert_within_tolerance(bf16_values(out), _masked_ref(d, mm), f"masked k={k} expected_m={expected_m}")
+        ref = _masked_ref(d, mm)
+        for major in ("K", "MN"):
+            out = _masked_call(d, major=major)
+            assert_within_tolerance(bf16_values(out), ref, f"masked k={k} expected_m={expected_m} {major}")
 
 
 def test_masked_expected_m_never_changes_results():
