@@ -275,10 +275,12 @@ def _bmm_scale(scale: torch.Tensor, batch: int, size: int, channel_shape, name: 
 
 
 def bmm_fp8(A: torch.Tensor, B: torch.Tensor, A_scale: torch.Tensor, B_scale: torch.Tensor, dtype: torch.dtype,
-            out: Optional[torch.Tensor] = None, backend: str = "auto") -> torch.Tensor:
+            out: Optional[torch.Tensor] = None, backend: str = "auto",
+            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Batched FP8 GEMM with the MATE page's parameters: A (batch,m,k), B (batch,k,n) E4M3; A_scale a
     scalar or (batch, m, 1), B_scale a scalar or (batch, 1, n); BF16 or FP16 output. The K-major copy
-    of B is made in a workspace allocated here."""
+    of B is made in ``workspace`` (uint8, at least batch*n*k bytes; an extension of the page's
+    signature), or in one taken from torch's caching allocator when it is None."""
     if backend != "auto":
         raise NotImplementedError("backend must be 'auto'")
     if A.dtype == torch.float8_e5m2 or B.dtype == torch.float8_e5m2:
@@ -291,5 +293,5 @@ def bmm_fp8(A: torch.Tensor, B: torch.Tensor, A_scale: torch.Tensor, B_scale: to
         if dtype not in _OUT_DTYPES:
             raise NotImplementedError(f"dtype {dtype} is not implemented (BF16 or FP16)")
         out = torch.empty((batch, m, n), dtype=dtype, device=A.device)
-    ws = torch.empty(max(1, batch * n * k), dtype=torch.uint8, device=A.device)
+    ws = workspace if workspace is not None else torch.empty(max(1, batch * n * k), dtype=torch.uint8, device=A.device)
     return fp8_bmm(A, B, sa, sb, out, ws, sa_rows, sb_cols)

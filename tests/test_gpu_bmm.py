@@ -74,3 +74,16 @@ def test_bmm_full_size_sampled():
         rows = np.unique(np.concatenate([[0, 255, 256, 1023], rng.choice(m, 6, replace=False)]))
         ref = obmm.bmm_fp8(a[g:g + 1, rows], b[g:g + 1], sa[g:g + 1, rows], sb[g:g + 1])[0]
         assert_within_tolerance(got[g, rows], ref, f"bmm full size batch {g}")
+
+
+def test_bmm_caller_workspace_matches_own():
+    """The MATE-signature call with a caller's workspace (reused over two calls, the second smaller)
+    gives the same values as the call that takes its own."""
+    ws = torch.empty(4 * 1040 * 384, dtype=torch.uint8, device=DEV)
+    for batch, m, n, k in [(4, 129, 1040, 384), (2, 37, 48, 256)]:
+        say("bmm caller workspace", batch, m, n, k)
+        d = workloads.bmm(batch, m, n, k, True, True, seed=7 + m, device=DEV)
+        own = fp8g.bmm_fp8(d["a"], d["b"], d["a_scale"], d["b_scale"], torch.bfloat16)
+        given = fp8g.bmm_fp8(d["a"], d["b"], d["a_scale"], d["b_scale"], torch.bfloat16, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(own, given)
