@@ -162,6 +162,58 @@ def test_results_do_not_depend_on_the_tile_configuration(form):
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
 
+@pytest.mark.parametrize("form", ["plain", "masked", "contiguous", "gathered"])
+def test_long_k_scale_ring_every_tile_and_layout(form):
+    """25 K blocks: a's row scales travel through their three-slot LDS ring in groups of 8 (4 on the
+    256x128 tile), so the ring wraps and every part phase and swizzle occurs. Every tile and both
+    scale layouts give one result, which matches the oracle."""
+    k = 25 * 128
+    say("long k scale ring", form, k)
+    if form == "plain":
+        d = workloads.plain(300, 384, k, seed=51, device=DEV)
+        ref = _plain_ref(d)
+        call = lambda major: _plain_call(d, major)
+    elif form == "masked":
+        mm = np.array([256, 70, 9], np.int32)
+        d = workloads.masked(3, 256, 256, k, 128, seed=52, device=DEV, masked_m=mm)
+        ref = _masked_ref(d, mm)
+        call = lambda major: _masked_call(d, major=major)
+    else:
+        d = workloads.contiguous(4, n=256, k=k, seed=53, device=DEV, counts=[200, 129, 0, 60])
+        ref = _contig_ref(d)
+        if form == "contiguous":
+            call = lambda major: _contig_call(d, major)
+        else:
+            # the same rows, gathered from a shuffled copy of a and of its scales
+            perm = np.random.default_rng(53).permutation(d["m"]).astype(np.int32)
+            inv = np.empty_like(perm)
+            inv[perm] = np.arange(d["m"], dtype=np.int32)
+            src = torch.from_numpy(perm).to(DEV).long()
+            a_src, sa_src = d["a"][src].contiguous(), d["a_scale"][src].contiguous()
+            rows = torch.from_numpy(inv).to(DEV)
+
+            def call(major):
+                sa, sb = sa_src, d["b_scale"]
+                if major == "MN":
+                    sa, sb = sa.t().contiguous(), sb.transpose(1, 2).contiguous()
+                out = sentinel_like((d["m"], d["n"]), DEV)
+                fp8g.fp8_group_gemm_contiguous_gather(a_src, sa, rows, d["b"], sb, d["m_indices"], out, major)
+                torch.cuda.synchronize()
+                return out
+    first, outs = None, []
+    try:
+        for tile in ("256x256", "128x256", "256x128", "128x128"):
+            os.environ["FP8G_TILE"] = tile
+            for major in ("K", "MN"):
+                out = call(major)
+                first = out if first is None else first
+                outs.append(host(out))
+    finally:
+        os.environ.pop("FP8G_TILE", None)
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+    assert_within_tolerance(bf16_values(first), ref, f"long k {form}")
+
+
 @pytest.mark.parametrize("form", ["plain", "contiguous", "masked"])
 def test_fp16_output_matches_oracle(form):
     """out_dtype FP16 (the page's other output type): same product, FP16 round-to-nearest-even."""
