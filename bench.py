@@ -24,8 +24,8 @@ algorithmic TFLOP/s, the fraction of its binding roofline, and the SHA-256 of it
 Configs 3-5 stream their weights from HBM, so each of their launches starts with cold caches (a
 512 MB read in between, not timed).
 
---extra adds the other workloads: the channelwise batched GEMM (8 x 1024x4096x7168, B transposed in
-the call), the add-RMSNorm + 1x128 quantiser and the plain quantiser over 4096x7168 BF16, the
+--extra adds the other workloads: the channelwise batched GEMM (8 x 1024x4096x7168, B read as
+(k, n) in place), the add-RMSNorm + 1x128 quantiser and the plain quantiser over 4096x7168 BF16, the
 per-tensor expert FFN, one GPU's share of the block-scale FFN under 8-way expert parallelism (8 of
 the 64 experts), and two context lines timed back to back like the headline: the per-tensor
 batched GEMM at batch 1 on the headline shape (the same matrix-core loop without per-block
@@ -301,23 +301,21 @@ def extra_configs(steps, warmup):
 
     d = workloads.bmm(8, 1024, 4096, 7168, True, True, seed=0, device=dev)
     out = torch.empty((8, 1024, 4096), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(8 * 4096 * 7168, dtype=torch.uint8, device=dev)
     sa, sb = d["a_scale"].reshape(8, 1024), d["b_scale"].reshape(8, 4096)
-    fn = lambda: fp8g.fp8_bmm(d["a"], d["b"], sa, sb, out, ws, True, True)
+    fn = lambda: fp8g.fp8_bmm(d["a"], d["b"], sa, sb, out, True, True)
     med, best = time_cold(fn, steps, warmup, flush)
     flops = 2.0 * 8 * 1024 * 4096 * 7168
     res["bmm_channelwise_8x1024x4096x7168"] = roofline_entry(med, best, flops, 8 * (1024 + 4096) * 7168 + 2 * 8 * 1024 * 4096)
-    del d, out, ws
+    del d, out
 
-    # The same matrix-core loop without per-block promotion (per-tensor scales, B transposed in the
-    # call) on the headline shape, and the vendor library's per-tensor FP8 GEMM (hipBLASLt through
+    # The same matrix-core loop without per-block promotion (per-tensor scales, B read as (k, n)) on
+    # the headline shape, and the vendor library's per-tensor FP8 GEMM (hipBLASLt through
     # torch._scaled_mm) on the same shape, for context: both back to back, like the headline.
     d = workloads.bmm(1, 4096, 4096, 7168, False, False, seed=0, device=dev)
     out = torch.empty((1, 4096, 4096), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(4096 * 7168, dtype=torch.uint8, device=dev)
     sa, sb = d["a_scale"].reshape(1), d["b_scale"].reshape(1)
     flops = 2.0 * 4096 * 4096 * 7168
-    ms, med, best, _, _ = time_launches(lambda: fp8g.fp8_bmm(d["a"], d["b"], sa, sb, out, ws, False, False), 50, 10)
+    ms, med, best, _, _ = time_launches(lambda: fp8g.fp8_bmm(d["a"], d["b"], sa, sb, out, False, False), 50, 10)
     res["bmm_tensorwise_1x4096x4096x7168"] = {"us_mean": round(ms * 1e3, 2), "tflops": round(flops / ms / 1e9, 2),
                                               "frac_mfma": round(flops / ms / 1e9 / FP8_DENSE_PEAK_TFLOPS, 4)}
     try:
@@ -330,7 +328,7 @@ def extra_configs(steps, warmup):
             "us_mean": round(ms * 1e3, 2), "tflops": round(flops / ms / 1e9, 2), "note": "vendor library, not this path"}
     except Exception as e:  # the reference is context only
         res["reference_hipblaslt_fp8_tensorwise_4096x4096x7168"] = {"error": f"{type(e).__name__}: {e}"[:200]}
-    del d, out, ws
+    del d, out
 
     d = workloads.norm(4096, 7168, seed=0, device=dev)
     res_t = d["residual"].clone()

@@ -202,16 +202,13 @@ FP8G_API fp8g_status_t fp8_batch_gemm_masked(const void* a, const void* b, const
  *   a_scale  FP32: one value (a_scale_per_row = 0) or (batch, m), one per row (= 1)
  *   b_scale  FP32: one value (b_scale_per_col = 0) or (batch, n), one per column (= 1)
  *   out      (batch, m, n) BF16 or FP16 (out_dtype), fully written
- *   workspace  device bytes, at least fp8_bmm_workspace_size(batch, n, k): b is first rewritten
- *              there as (batch, n, k), so that the matrix cores read both operands K-major
- * The k-sum is accumulated in FP32 over all of k, then multiplied by the FP32 product of the two
- * scales. k is a multiple of 128 and n of 16; m is arbitrary; batch <= 65535. E4M3 only.
+ * b is read in place (no copy, no workspace). The k-sum is accumulated in FP32 over all of k, then
+ * multiplied by the FP32 product of the two scales. k is a multiple of 128 and n of 16; m is
+ * arbitrary; batch <= 65535. E4M3 only.
  */
-FP8G_API int64_t fp8_bmm_workspace_size(int64_t batch, int64_t n, int64_t k);
 FP8G_API fp8g_status_t fp8_bmm(const void* a, const void* b, const float* a_scale, int32_t a_scale_per_row,
                       const float* b_scale, int32_t b_scale_per_col, void* out, int32_t out_dtype,
-                      int64_t batch, int64_t m, int64_t n, int64_t k, void* workspace,
-                      int64_t workspace_bytes, void* stream);
+                      int64_t batch, int64_t m, int64_t n, int64_t k, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Producers of the a operand (1x128 E4M3 rows with FP32 scales).

@@ -35,8 +35,7 @@ SIGNATURES = {
                                           _I32, _I32, _P], _I32),
     "fp8_batch_gemm_masked": ([_P, _P, _P, _P, _P, _I64, _P, _I32, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32,
                                _P], _I32),
-    "fp8_bmm_workspace_size": ([_I64, _I64, _I64], _I64),
-    "fp8_bmm": ([_P, _P, _P, _I32, _P, _I32, _P, _I32, _I64, _I64, _I64, _I64, _P, _I64, _P], _I32),
+    "fp8_bmm": ([_P, _P, _P, _I32, _P, _I32, _P, _I32, _I64, _I64, _I64, _I64, _P], _I32),
     "fp8_quantize_1x128": ([_P, _I64, _I64, _P, _P, _I32, _P], _I32),
     "fp8_fused_add_rmsnorm_quant": ([_P, _P, _P, _P, _P, _P, ctypes.c_float, _I64, _I64, _I32, _P], _I32),
     "fp8_moe_permutation_workspace_size": ([_I64, _I64, _I64], _I64),

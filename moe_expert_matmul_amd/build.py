@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libfp8g.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 POISON_LIB_PATH = os.path.join(PKG_DIR, "libfp8g_poison_lds.so")  # debug build, NaN-poisoned LDS
-SOURCES = ["api.hip", "gemm.hip", "moe.hip", "quant.hip", "bmm.hip", "clock.hip"]
+SOURCES = ["api.hip", "gemm.hip", "moe.hip", "quant.hip", "clock.hip"]
 
 ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -628,14 +628,9 @@ fp8g_status_t fp8_moe_gather_quant(const void* x, const int32_t* src_token, int6
   });
 }
 
-int64_t fp8_bmm_workspace_size(int64_t batch, int64_t n, int64_t k) {
-  if (batch < 0 || n < 0 || k < 0) return -1;
-  return batch * n * k;
-}
-
 fp8g_status_t fp8_bmm(const void* a, const void* b, const float* a_scale, int32_t a_scale_per_row,
                       const float* b_scale, int32_t b_scale_per_col, void* out, int32_t out_dtype, int64_t batch,
-                      int64_t m, int64_t n, int64_t k, void* workspace, int64_t workspace_bytes, void* stream) {
+                      int64_t m, int64_t n, int64_t k, void* stream) {
   return guarded([&] {
     require(batch >= 0 && batch <= 65535, "batch (%lld) must be in [0, 65535]", (long long)batch);
     check_gemm_dims(m, n, k, /*n_tail=*/true);
@@ -647,20 +642,13 @@ fp8g_status_t fp8_bmm(const void* a, const void* b, const float* a_scale, int32_
     require(mul_sat(batch, mul_sat(m, n)) <= ((int64_t)1 << 40) && mul_sat(batch, mul_sat(n, k)) <= ((int64_t)1 << 40),
             "sizes too large");
     require(out && a_scale && b_scale, "out and the scales must be non-null");
-    require(k == 0 || (a && b && workspace), "a, b and the workspace must be non-null");
-    require(workspace_bytes >= batch * n * k, "workspace (%lld bytes) must hold batch*n*k = %lld bytes",
-            (long long)workspace_bytes, (long long)(batch * n * k));
-    require(aligned(a, 16) && aligned(b, 16) && aligned(out, 16) && aligned(workspace, 16),
-            "a, b, out and the workspace must be 16-byte aligned");
+    require(k == 0 || (a && b), "a and b must be non-null");
+    require(aligned(a, 16) && aligned(b, 16) && aligned(out, 16), "a, b and out must be 16-byte aligned");
     require(aligned(a_scale, 4) && aligned(b_scale, 4), "scales must be 4-byte aligned");
     check_device();
-    if (k > 0)
-      check_hip(fp8g::launch_transpose_bytes(static_cast<const uint8_t*>(b), (int)batch, (int)k, (int)n,
-                                             static_cast<uint8_t*>(workspace), (hipStream_t)stream),
-                "fp8_bmm transpose launch");
     fp8g::GemmParams p{};
     p.a = static_cast<const uint8_t*>(a);
-    p.b = static_cast<const uint8_t*>(workspace);
+    p.b = static_cast<const uint8_t*>(b);
     p.sa = a_scale;
     p.sb = b_scale;
     p.out = static_cast<uint16_t*>(out);

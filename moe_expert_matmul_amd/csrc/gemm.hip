@@ -250,6 +250,9 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
   constexpr bool CONTIG = MODE == MODE_CONTIG || MODE == MODE_CONTIG_SWIGLU || PT;
   constexpr bool SWIGLU = MODE == MODE_CONTIG_SWIGLU || MODE == MODE_CONTIG_PT_SWIGLU;
   constexpr bool NO_PROMOTION = MODE == MODE_BMM || PT;  // scales constant along K: applied at the end
+  // bmm_fp8 takes b as (batch, k, n): its slabs are k rows of the tile's columns, read into
+  // fragments by transposing LDS reads (load_frag_kn)
+  constexpr bool B_KMAJOR = MODE == MODE_BMM;
   // Split pipeline (the masked form's two-stage tiles): one a buffer and three b slots. Iteration
   // kb computes block kb; once every wave has read its a fragments of block kb (a second barrier,
   // mid-block), the a slabs of block kb+1 are loaded into the a buffer, and the b slabs and scales
@@ -430,12 +433,25 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     if (!((a_live_bits >> q) & 1)) a_off[q] = 0x80000000u;
 #pragma unroll
   for (int q = 0; q < T::B_LOADS; ++q) {
-    const int slab_row = (wave * T::B_LOADS + q) * SLAB_ROWS;
-    const int lchunk = (lane & 7) ^ swizzle(slab_row + lrow);
-    int r = min(col0 + slab_row + lrow, p.n - 1);
-    if (SWIGLU) r = swiglu_b_row(slab_row + lrow);
-    b_off[q] = (uint32_t)r * (uint32_t)p.k + lchunk * 16;
+    if constexpr (B_KMAJOR) {
+      // Slab s of the k-major tile holds k rows [KN_ROWS s, KN_ROWS s + KN_ROWS); lane l fills its
+      // chunk l: row KN_ROWS s + l / KN_CHUNKS at physical chunk l % KN_CHUNKS, which holds logical
+      // chunk (l % KN_CHUNKS) ^ kn_swizzle(row), columns col0 + 16 * that. Chunks past n (n is a
+      // multiple of 16) re-read the last chunk; those columns are never stored.
+      constexpr int KN_CHUNKS = BN / 16, KN_ROWS = 64 / KN_CHUNKS;
+      const int kr = (wave * T::B_LOADS + q) * KN_ROWS + lane / KN_CHUNKS;
+      const int lchunk = (lane % KN_CHUNKS) ^ kn_swizzle<BN>(kr);
+      b_off[q] = (uint32_t)kr * (uint32_t)p.n + (uint32_t)min(col0 + lchunk * 16, p.n - 16);
+    } else {
+      const int slab_row = (wave * T::B_LOADS + q) * SLAB_ROWS;
+      const int lchunk = (lane & 7) ^ swizzle(slab_row + lrow);
+      int r = min(col0 + slab_row + lrow, p.n - 1);
+      if (SWIGLU) r = swiglu_b_row(slab_row + lrow);
+      b_off[q] = (uint32_t)r * (uint32_t)p.k + lchunk * 16;
+    }
   }
+  // byte step of b's slabs from one K block to the next
+  const uint32_t b_kb_step = B_KMAJOR ? (uint32_t)KBLK * (uint32_t)p.n : (uint32_t)KBLK;
 
   // Buffer resources of this tile's operands (per group for the grouped forms).
   const uint8_t* B = p.b + (int64_t)bsel * p.b_group_stride;
@@ -546,7 +562,7 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     load_lds_16(rA_it, a_stage(kb) + (wave * T::A_LOADS + q) * 1024, a_off[q], (uint32_t)kb * KBLK);
   };
   auto issue_b = [&](int kb, int q) {
-    load_lds_16(rB_it, b_stage(kb) + (wave * T::B_LOADS + q) * 1024, b_off[q], (uint32_t)kb * KBLK);
+    load_lds_16(rB_it, b_stage(kb) + (wave * T::B_LOADS + q) * 1024, b_off[q], (uint32_t)kb * b_kb_step);
   };
   auto issue_s = [&](int kb) {
     const int qq = kb & (SGRP - 1), grp = kb / SGRP + 1;
@@ -630,22 +646,30 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     i32x8 af[T::IG];
 #pragma unroll
     for (int ig = 0; ig < T::IG; ++ig) af[ig] = load_frag(sA, i0 + ig * 16 + fr, lane);
+    // b's fragment of column group jg (k-major b: four transposing reads instead of two)
+    auto b_frag = [&](int jg) {
+      if constexpr (B_KMAJOR)
+        return load_frag_kn<BN>(sB, j0 + jg * 16, lane);
+      else
+        return load_frag(sB, j0 + jg * 16 + fr, lane);
+    };
+    constexpr int B_FRAG_READS = B_KMAJOR ? 4 : 2;
     i32x8 bq[T::JG];
 #pragma unroll
-    for (int jg = 0; jg < BPRE && jg < T::JG; ++jg) bq[jg] = load_frag(sB, j0 + jg * 16 + fr, lane);
+    for (int jg = 0; jg < BPRE && jg < T::JG; ++jg) bq[jg] = b_frag(jg);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int jg = 0; jg < T::JG; ++jg) {
 #pragma unroll
       for (int i = load_first(jg); i < load_first(jg + 1); ++i) issue_load(kb_load, i);
-      if (jg + BPRE < T::JG) bq[jg + BPRE] = load_frag(sB, j0 + (jg + BPRE) * 16 + fr, lane);
+      if (jg + BPRE < T::JG) bq[jg + BPRE] = b_frag(jg + BPRE);
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ig = 0; ig < T::IG; ++ig)
         acc[ig][jg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bq[jg], af[ig], acc[ig][jg], FMT_E4M3, FMT_E4M3,
                                                                       0, E8M0_ONE, 0, E8M0_ONE);
       sched_vmem_group(load_first(jg + 1) - load_first(jg));
-      if (jg + BPRE < T::JG) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+      if (jg + BPRE < T::JG) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, B_FRAG_READS, 0);
       __builtin_amdgcn_sched_group_barrier(SG_MFMA, T::IG, 0);
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);

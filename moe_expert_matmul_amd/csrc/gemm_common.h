@@ -145,5 +145,42 @@ __device__ __forceinline__ i32x8 load_frag(const uint8_t* slab, int row, int lan
   return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
+// ---- operand b stored k-major (n contiguous in memory), as bmm_fp8 takes it ----------------
+// In LDS the K block is 128 rows of BN bytes (one row per k, BN consecutive columns); the 16-byte
+// chunk c of row k sits at c ^ kn_swizzle(k). The fragment reads below (ds_read_b64_tr_b8) have
+// each half-wave read 16 bytes from each of 16 rows {k0 + r, k0 + 16 + r : r < 8} at one logical
+// chunk; the swizzle gives those 16 rows 16 distinct bank positions (BN = 256: 16 chunks per
+// 64-bank row; BN = 128: two rows per 64 banks, 8 chunks each, rows of one parity distinct).
+template <int BN>
+__device__ __forceinline__ int kn_swizzle(int k) {
+  static_assert(BN == 128 || BN == 256, "k-major b tiles are 128 or 256 columns wide");
+  return BN == 256 ? (k & 7) | ((k >> 1) & 8) : ((k >> 1) & 3) | ((k >> 2) & 4);
+}
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// Eight k of one column per lane: ds_read_b64_tr_b8 takes, in each 16-lane group, 8 bytes from
+// every lane (lane 2r + h: bytes 8h .. 8h+7 of row r's 16 columns) and returns to lane c the byte of
+// column c from each of the 8 rows, row 0 in the lowest byte.
+// The pointer is __restrict__ so that the read carries alias information, as the plain LDS reads
+// do: without it the compiler makes the read wait for every slab load in flight (vmcnt(0)), the
+// next stage's included. The pipeline's own waits and barriers order the reads after their slabs.
+__device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(p));
+}
+
+// The fragment load_frag gives for b rows col .. col+15 (lane l: column col + (l & 15), k bytes
+// 16g .. 16g+15 and 64+16g .. 64+16g+15 of the block, g = l >> 4), read from a k-major slab with
+// four transposing reads of 8 k each.
+template <int BN>
+__device__ __forceinline__ i32x8 load_frag_kn(const uint8_t* slab, int col, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  const int c = col >> 4;
+  const int r = i >> 1, h8 = (i & 1) * 8;
+  auto rd = [&](int k) { return lds_read_tr8(slab + k * BN + ((c ^ kn_swizzle<BN>(k)) << 4) + h8); };
+  const i32x2 x0 = rd(16 * g + r), x1 = rd(16 * g + 8 + r), x2 = rd(64 + 16 * g + r), x3 = rd(64 + 16 * g + 8 + r);
+  return i32x8{x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
+}
+
 }  // namespace kernels
 }  // namespace fp8g

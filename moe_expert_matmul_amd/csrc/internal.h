@@ -12,7 +12,7 @@ enum GemmMode : int {
   MODE_CONTIG = 1,  // per 128-row tile, b chosen by the tile's expert in m_indices
   MODE_MASKED = 2,  // per group g, rows below masked_m[g]
   MODE_CONTIG_SWIGLU = 3,  // contiguous, epilogue silu(gate) * up -> 1x128 E4M3 (expert-FFN fc1)
-  MODE_BMM = 4,     // per batch g: out = sa * sb * (a @ b.T), scales per tensor or per row / column
+  MODE_BMM = 4,     // per batch g: out = sa * sb * (a @ b), b (k, n); scales per tensor or per row / column
   MODE_CONTIG_PT = 5,         // contiguous, out = group_dequant[e] * (a @ b[e].T) (per-tensor FP8)
   MODE_CONTIG_PT_SWIGLU = 6,  // contiguous per-tensor, epilogue E4M3(silu(gate) * up * act_quant)
 };
@@ -78,8 +78,6 @@ int tile_cols(TileConfig cfg);
 
 hipError_t launch_gemm(GemmMode mode, TileConfig cfg, GemmParams p, int grid, hipStream_t stream);
 
-hipError_t launch_transpose_bytes(const uint8_t* src, int batch, int rows, int cols, uint8_t* dst,
-                                  hipStream_t stream);
 hipError_t launch_quantize_rows_1x128(const uint16_t* x, const int32_t* src_row, int num_src, int rows, int cols,
                                       uint8_t* out, float* scale_out, bool mn_major, hipStream_t stream);
 hipError_t launch_quantize_1x128(const uint16_t* x, int rows, int cols, uint8_t* out, float* scale_out,

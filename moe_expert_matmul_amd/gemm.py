@@ -237,9 +237,9 @@ def batch_deepgemm_fp8_nt_groupwise(a: torch.Tensor, b: torch.Tensor, a_scale: t
                                  tuple(scale_granularity_mnk))
 
 
-def fp8_bmm(a, b, a_scale, b_scale, out, workspace, a_scale_per_row: bool, b_scale_per_col: bool) -> torch.Tensor:
+def fp8_bmm(a, b, a_scale, b_scale, out, a_scale_per_row: bool, b_scale_per_col: bool) -> torch.Tensor:
     """out (batch,m,n) = sa * sb * (a (batch,m,k) @ b (batch,k,n)); a_scale is one value or (batch, m),
-    b_scale one value or (batch, n); workspace holds at least batch*n*k bytes."""
+    b_scale one value or (batch, n). b is read in place."""
     dev = _require_cuda(a)
     batch, m, k = a.shape
     n = b.shape[2]
@@ -253,14 +253,9 @@ def fp8_bmm(a, b, a_scale, b_scale, out, workspace, a_scale_per_row: bool, b_sca
         raise ValueError("a per-tensor b_scale holds one value")
     _check(out, "out", _OUT_DTYPES, (batch, m, n), dev)
     lib = _lib.load()
-    need = lib.fp8_bmm_workspace_size(batch, n, k)
-    if not (isinstance(workspace, torch.Tensor) and workspace.device == dev and workspace.is_contiguous()
-            and workspace.numel() * workspace.element_size() >= need):
-        raise ValueError(f"workspace must be a contiguous device tensor of at least {need} bytes")
     with torch.cuda.device(dev):
         st = lib.fp8_bmm(_ptr(a), _ptr(b), _ptr(a_scale), int(bool(a_scale_per_row)), _ptr(b_scale),
-                         int(bool(b_scale_per_col)), _ptr(out), _out_code(out), batch, m, n, k, _ptr(workspace),
-                         workspace.numel() * workspace.element_size(), _stream(dev))
+                         int(bool(b_scale_per_col)), _ptr(out), _out_code(out), batch, m, n, k, _stream(dev))
     _lib.check(st, "fp8_bmm")
     return out
 
@@ -275,12 +270,10 @@ def _bmm_scale(scale: torch.Tensor, batch: int, size: int, channel_shape, name: 
 
 
 def bmm_fp8(A: torch.Tensor, B: torch.Tensor, A_scale: torch.Tensor, B_scale: torch.Tensor, dtype: torch.dtype,
-            out: Optional[torch.Tensor] = None, backend: str = "auto",
-            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+            out: Optional[torch.Tensor] = None, backend: str = "auto") -> torch.Tensor:
     """Batched FP8 GEMM with the MATE page's parameters: A (batch,m,k), B (batch,k,n) E4M3; A_scale a
-    scalar or (batch, m, 1), B_scale a scalar or (batch, 1, n); BF16 or FP16 output. The K-major copy
-    of B is made in ``workspace`` (uint8, at least batch*n*k bytes; an extension of the page's
-    signature), or in one taken from torch's caching allocator when it is None."""
+    scalar or (batch, m, 1), B_scale a scalar or (batch, 1, n); BF16 or FP16 output. With ``out``
+    given, nothing is allocated (scales already FP32 and contiguous are used as they are)."""
     if backend != "auto":
         raise NotImplementedError("backend must be 'auto'")
     if A.dtype == torch.float8_e5m2 or B.dtype == torch.float8_e5m2:
@@ -293,5 +286,4 @@ def bmm_fp8(A: torch.Tensor, B: torch.Tensor, A_scale: torch.Tensor, B_scale: to
         if dtype not in _OUT_DTYPES:
             raise NotImplementedError(f"dtype {dtype} is not implemented (BF16 or FP16)")
         out = torch.empty((batch, m, n), dtype=dtype, device=A.device)
-    ws = workspace if workspace is not None else torch.empty(max(1, batch * n * k), dtype=torch.uint8, device=A.device)
-    return fp8_bmm(A, B, sa, sb, out, ws, sa_rows, sb_cols)
+    return fp8_bmm(A, B, sa, sb, out, sa_rows, sb_cols)

@@ -71,12 +71,12 @@ int main(void) {
   EXPECT(fp8_batch_gemm_masked(p, p, f, f, ip, 8, p, 0, 2, huge, huge, 128, 0, 1, 128, 128, NULL), INV);
   EXPECT(fp8_batch_gemm_masked(p, p, f, f, ip, 8, p, 0, 0, 64, 128, 128, 0, 1, 128, 128, NULL), OK);
   /* bmm */
-  EXPECT(fp8_bmm(p, p, f, 0, f, 0, p, 0, 2, 64, 100, 128, p, 1 << 20, NULL), INV);
-  EXPECT(fp8_bmm(p, p, f, 0, f, 0, p, 0, 2, 64, 128, 128, p, 10, NULL), INV);
-  EXPECT(fp8_bmm(p, p, f, 2, f, 0, p, 0, 2, 64, 128, 128, p, 1 << 20, NULL), INV);
-  EXPECT(fp8_bmm(p, p, f, 0, f, 0, p, 0, 70000, 64, 128, 128, p, 1 << 20, NULL), INV);
-  EXPECT(fp8_bmm(p, p, f, 0, f, 0, p, 0, 2, huge, huge, 128, p, 1 << 20, NULL), INV);
-  if (fp8_bmm_workspace_size(neg, 1, 1) != -1 || fp8_bmm_workspace_size(2, 3, 128) != 768) return 3;
+  EXPECT(fp8_bmm(p, p, f, 0, f, 0, p, 0, 2, 64, 100, 128, NULL), INV);
+  EXPECT(fp8_bmm(p, p, f, 0, f, 0, p, 0, 2, 64, 128, 100, NULL), INV);
+  EXPECT(fp8_bmm(p, p, f, 2, f, 0, p, 0, 2, 64, 128, 128, NULL), INV);
+  EXPECT(fp8_bmm(p, p, f, 0, f, 0, p, 0, 70000, 64, 128, 128, NULL), INV);
+  EXPECT(fp8_bmm(p, p, f, 0, f, 0, p, 0, 2, huge, huge, 128, NULL), INV);
+  EXPECT(fp8_bmm(p, NULL, f, 0, f, 0, p, 0, 2, 64, 128, 128, NULL), INV);
   /* producers */
   EXPECT(fp8_quantize_1x128(p, 4, 100, p, (float*)f, 0, NULL), INV);
   EXPECT(fp8_quantize_1x128(p, huge, huge * 128, p, (float*)f, 0, NULL), INV);

@@ -76,14 +76,21 @@ def test_bmm_full_size_sampled():
         assert_within_tolerance(got[g, rows], ref, f"bmm full size batch {g}")
 
 
-def test_bmm_caller_workspace_matches_own():
-    """The MATE-signature call with a caller's workspace (reused over two calls, the second smaller)
-    gives the same values as the call that takes its own."""
-    ws = torch.empty(4 * 1040 * 384, dtype=torch.uint8, device=DEV)
+def test_bmm_with_out_allocates_nothing_and_leaves_b_alone():
+    """With out given and FP32 scales, the MATE-signature call allocates no device memory (b is read
+    in place, as (batch, k, n)), leaves b unchanged, and gives the values of the call that
+    allocates its own out; over two calls, the second smaller."""
     for batch, m, n, k in [(4, 129, 1040, 384), (2, 37, 48, 256)]:
-        say("bmm caller workspace", batch, m, n, k)
+        say("bmm allocation-free", batch, m, n, k)
         d = workloads.bmm(batch, m, n, k, True, True, seed=7 + m, device=DEV)
+        b_before = d["b"].clone()
         own = fp8g.bmm_fp8(d["a"], d["b"], d["a_scale"], d["b_scale"], torch.bfloat16)
-        given = fp8g.bmm_fp8(d["a"], d["b"], d["a_scale"], d["b_scale"], torch.bfloat16, workspace=ws)
+        out = torch.empty_like(own)
         torch.cuda.synchronize()
-        assert torch.equal(own, given)
+        torch.cuda.reset_peak_memory_stats()
+        before = torch.cuda.memory_allocated()
+        fp8g.bmm_fp8(d["a"], d["b"], d["a_scale"], d["b_scale"], torch.bfloat16, out=out)
+        torch.cuda.synchronize()
+        assert torch.cuda.max_memory_allocated() == before
+        assert torch.equal(own, out)
+        assert torch.equal(d["b"], b_before)

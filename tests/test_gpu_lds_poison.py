@@ -100,10 +100,8 @@ def test_fused_fc1_and_bmm_same_bytes_with_poisoned_lds():
 
     def bmm(lib):
         out = torch.empty((2, 256, 512), dtype=torch.bfloat16, device=DEV)
-        ws_b = torch.empty(2 * 512 * 1024, dtype=torch.uint8, device=DEV)
         _lib.check(lib.fp8_bmm(b["a"].data_ptr(), b["b"].data_ptr(), b["a_scale"].data_ptr(), 1,
-                               b["b_scale"].data_ptr(), 1, out.data_ptr(), 0, 2, 256, 512, 1024, ws_b.data_ptr(),
-                               ws_b.numel(), _stream()), "bmm")
+                               b["b_scale"].data_ptr(), 1, out.data_ptr(), 0, 2, 256, 512, 1024, _stream()), "bmm")
         return out
     ref, got = _both(bmm)
     assert np.array_equal(ref, got)
