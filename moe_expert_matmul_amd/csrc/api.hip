@@ -161,6 +161,12 @@ int fp8g::group_m_override(int group_m) {
   return v > 0 ? v : group_m;
 }
 
+int fp8g::group_n_override(int group_n) {
+  const char* e = std::getenv("FP8G_GROUP_N");
+  if (!e) return group_n;
+  return std::atoi(e);
+}
+
 int fp8g::tile_override() {
   const char* e = std::getenv("FP8G_TILE");
   if (!e) return -1;
@@ -385,10 +391,18 @@ void group_gemm_contiguous(const void* a, const float* a_scale, int64_t a_src_ro
   if (swiglu && fp8g::tile_cols(cfg) != 256) cfg = fp8g::TILE_128x256;  // gate and up share a 256-wide tile
   p.tiles_m = (int32_t)(ceil_div(m, fp8g::tile_rows(cfg)) * (fp8g::tile_rows(cfg) / 128));
   p.tiles_n = swiglu ? (int32_t)(n / 256) : (int32_t)ceil_div(n, fp8g::tile_cols(cfg));
-  // 128-row tiles: the row tiles of one column tile run together and share b's slab in L2.
+  // 128-row tiles with a gathered a (the expert FFN's fc1): the row tiles of one column tile run
+  // together and share b's slab in L2; a's rows come from the much smaller token matrix, whose
+  // re-reads hit in cache. 128-row tiles with a read in place: bands of 8 column tiles, so an
+  // XCD's 32 workgroups are 4 row tiles x 8 column tiles that share both a's rows and b's slabs
+  // in L2 (a is otherwise re-read once per column tile). Measured against the column order: 32
+  // Zipf experts x 8192 rows (n 4096, k 7168) 343 against 363 us, 64 x 512 rows 1045 against
+  // 1115, 64 Zipf x 16384 660 against 733, k 2048 / n 7168 199 against 208; the gathered fc1
+  // 1393-1402 against 1304 us, so it keeps the column order.
   // 256-row tiles: the column tiles of one row tile run together and share a's rows in L2 (each
   // expert's weights are streamed once either way); measured 1.8x faster for them.
   p.group_m = fp8g::group_m_override(fp8g::tile_rows(cfg) == 256 ? 1 : p.tiles_m);
+  p.group_n = fp8g::group_n_override(a_rows == nullptr && fp8g::tile_rows(cfg) == 128 ? 8 : 0);
   const int64_t grid = mul_sat(p.tiles_m, p.tiles_n);
   require(grid <= kInt32Max, "too many tiles");
   const fp8g::GemmMode mode = pt ? (swiglu ? fp8g::MODE_CONTIG_PT_SWIGLU : fp8g::MODE_CONTIG_PT)

@@ -302,6 +302,8 @@ gemm_fp8_groupwise_kernel(const GemmParams p) {
     xcd_row_interleave(blockIdx.x, p.tiles_m / 2, 2 * p.tiles_n, tm, k);
     half = k / p.tiles_n;
     tn = k - half * p.tiles_n;
+  } else if (p.group_n > 0) {
+    raster(t, p.tiles_n, p.tiles_m, p.group_n, tn, tm);
   } else {
     raster(t, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
   }

@@ -52,6 +52,9 @@ struct GemmParams {
   int32_t sb_nb_stride, sb_kb_stride;   // b_scale element of (n block, kb)
   int32_t num_groups;
   int32_t tiles_m, tiles_n, group_m;
+  // group_n > 0: tiles are rastered in bands of group_n column tiles (consecutive tiles walk the
+  // band's column tiles for one row tile, then the next row tile); else in bands of group_m row tiles
+  int32_t group_n;
 };
 
 // Tile configurations the host may pick. Results are identical for every configuration.
@@ -72,6 +75,9 @@ int tile_override();
 // Row tiles per raster group, forced through the FP8G_GROUP_M environment variable (a positive
 // integer), read at every call; `group_m` when unset. Tile order only: results never change.
 int group_m_override(int group_m);
+// Column tiles per raster band (GemmParams::group_n), forced through FP8G_GROUP_N (0 turns the
+// bands off), read at every call; `group_n` when unset. Tile order only: results never change.
+int group_n_override(int group_n);
 
 int tile_rows(TileConfig cfg);
 int tile_cols(TileConfig cfg);

@@ -162,6 +162,25 @@ def test_results_do_not_depend_on_the_tile_configuration(form):
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
 
+@pytest.mark.parametrize("n", [2048, 1152, 256])
+def test_contiguous_tile_order_does_not_change_results(n):
+    """The contiguous form's tile order (row-tile groups, or bands of column tiles whose width
+    need not divide the column tiles) only changes which workgroup computes a tile: every order
+    gives the same bytes, with every valid row written (the output starts as NaN sentinels)."""
+    say("contiguous tile order", n)
+    d = workloads.contiguous(7, n=n, k=256, seed=61, device=DEV, counts=[300, 0, 513, 40, 128, 1000, 77])
+    outs = []
+    try:
+        for gn in ("0", "1", "3", "8", "16"):
+            os.environ["FP8G_GROUP_N"] = gn
+            outs.append(host(_contig_call(d)))
+    finally:
+        os.environ.pop("FP8G_GROUP_N", None)
+    valid = host(d["m_indices"]) >= 0
+    assert not (outs[0][valid] == 0x7FC1).any()  # bf16 bit patterns: no valid row left unwritten
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
 @pytest.mark.parametrize("form", ["plain", "masked", "contiguous", "gathered"])
 def test_long_k_scale_ring_every_tile_and_layout(form):
     """25 K blocks: a's row scales travel through their three-slot LDS ring in groups of 8 (4 on the
