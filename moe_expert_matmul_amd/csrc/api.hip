@@ -397,8 +397,10 @@ void group_gemm_contiguous(const void* a, const float* a_scale, int64_t a_src_ro
   // XCD's 32 workgroups are 4 row tiles x 8 column tiles that share both a's rows and b's slabs
   // in L2 (a is otherwise re-read once per column tile). Measured against the column order: 32
   // Zipf experts x 8192 rows (n 4096, k 7168) 343 against 363 us, 64 x 512 rows 1045 against
-  // 1115, 64 Zipf x 16384 660 against 733, k 2048 / n 7168 199 against 208; the gathered fc1
-  // 1393-1402 against 1304 us, so it keeps the column order.
+  // 1115, 64 Zipf x 16384 660 against 733, k 2048 / n 7168 199 against 208, and 2-4% on experts
+  // whose row tiles straddle the bands (64 x 576 or 520 rows, 32 x 300, 8 x 2000); the gathered
+  // fc1 1393-1402 against 1304 us, so it keeps the column order. (The expert FFN's fc2, k 2048,
+  // takes 256-row tiles; on 128-row tiles it measured 735 with bands against 686 us.)
   // 256-row tiles: the column tiles of one row tile run together and share a's rows in L2 (each
   // expert's weights are streamed once either way); measured 1.8x faster for them.
   p.group_m = fp8g::group_m_override(fp8g::tile_rows(cfg) == 256 ? 1 : p.tiles_m);
