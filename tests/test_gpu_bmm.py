@@ -16,7 +16,10 @@ from parity import assert_within_tolerance, bf16_values, fp16_values, host, say,
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
-CASES = [(1, 1, 16, 128), (3, 37, 48, 256), (2, 300, 272, 512), (4, 129, 1040, 384), (8, 1000, 512, 1024)]
+# b is read as (k, n) slabs of the tile's columns: n below one tile (16, 48, 128), a last tile with
+# one 16-column chunk (4112 = 16 * 257), and 25 K blocks
+CASES = [(1, 1, 16, 128), (3, 37, 48, 256), (2, 64, 128, 256), (2, 300, 272, 512), (4, 129, 1040, 384),
+         (8, 1000, 512, 1024), (1, 17, 4112, 3200)]
 
 
 def _ref(d):
