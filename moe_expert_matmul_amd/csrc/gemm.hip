@@ -40,7 +40,8 @@
 //                          epilogue (flashinfer-rs README, "API Example: Fused MoE FP8 (cudarc)");
 //   BMM                    bmm_fp8 of the MATE page: per-tensor or per-row/column scales, so each
 //                          MFMA accumulates straight into the sum over all of K and the scales are
-//                          applied once in the epilogue;
+//                          applied once in the epilogue; b is read as the caller gives it, (k, n)
+//                          with n contiguous, as slabs of k rows (see load_frag_kn);
 //   CONTIG_PT(_SWIGLU)     the README's per-tensor FP8 FFN: the BMM loop under the contiguous
 //                          scheduler, one dequantisation scale per expert.
 #include "gemm_common.h"
