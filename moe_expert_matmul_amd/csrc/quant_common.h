@@ -24,14 +24,6 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4 raw, float v[8]) {
   }
 }
 
-// 16 bytes read once by this kernel and by nothing after it: a non-temporal load, so the stream
-// does not displace cache lines that later kernels will read.
-__device__ __forceinline__ uint4 load_once_16(const void* p) {
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
