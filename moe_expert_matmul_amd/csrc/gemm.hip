@@ -15,8 +15,9 @@
 // contiguous bytes of a row.
 //
 // Data movement per workgroup and K block: the BMx128 slab of a and the BNx128 slab of b go from
-// HBM straight into LDS (global_load_lds_dwordx4, no VGPR staging), double-buffered so the loads of
-// block kb+1 overlap the MFMAs of block kb. Rows are 128 bytes in LDS with their 16-byte chunks
+// HBM straight into LDS (global_load_lds_dwordx4, no VGPR staging), in two to four stages so the
+// loads of the next blocks overlap the MFMAs of block kb (the masked form: one a buffer and three
+// b slots, see SPLIT below). Rows are 128 bytes in LDS with their 16-byte chunks
 // XOR-swizzled by ((row >> 1) & 7), which spreads the 16 rows of a fragment over all 64 four-byte
 // banks; together with the fragment's chunk assignment (see load_frag) a fragment read runs at the
 // LDS's full rate. The swizzle is applied on the global side: lane l of a load writes LDS chunk l of
@@ -28,9 +29,12 @@
 //
 // Tile scheduling: the 1-D grid is renumbered so that consecutive tiles run on the same XCD (the
 // hardware deals workgroups round-robin over the 8 XCDs, each with its own L2) and then rasterised
-// in groups of `group_m` row tiles. The masked form maps the grid to (group, row tile, col tile) and
-// drops tiles at or beyond masked_m[g]; the contiguous form reads the tile's 128 m_indices and drops
-// tiles that hold only padding. Rows that are not valid are still computed when they share a wave
+// in groups of `group_m` row tiles, or, for the contiguous form's 128-row tiles with a read in
+// place, in bands of `group_n` column tiles. The masked form maps the grid to (group, row tile,
+// col tile) and drops tiles at or beyond masked_m[g]; the contiguous form reads the tile's
+// m_indices and drops tiles that hold only padding. With 256-row tiles the contiguous grid has two
+// entries per tile, one per 128-row half, dealt to the XCDs by tile row: a tile whose halves hold
+// one expert runs as its first entry, one whose halves hold two experts as two. Rows that are not valid are still computed when they share a wave
 // with valid rows (each output row depends only on its own a row and scale) but never stored.
 //
 // Modes (the MODE template argument) on the same loop:
